@@ -1,0 +1,285 @@
+/*
+ * rmm_oracle.c -- reference ("oracle") implementation of Reduced Matrix
+ * Multiplication (RMM).
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark are the only users of this library.  The
+ * GPU library (input_adaptive_reduced_02_amd/) never includes, links or calls
+ * it, and the two share no code, header, table or helper.
+ *
+ * Plain, slow, single-threaded C.  All arithmetic is IEEE binary64, built with
+ * -O2 -ffp-contract=off so that every a*b + c rounds twice, exactly as
+ * written.  Callers pass the exact values the GPU consumes (bf16 or fp32 bit
+ * patterns widened to double).
+ *
+ * Source: "Reduced Matrix Multiplication: Input-Adaptive Matrix-Product
+ * Reduction for LLM Inference" (Lan, Li, Zhou), technical summary on
+ * gist.science, section "Metodologia":
+ *   - every Transformer matmul is read as Y = A B, A being the activation and
+ *     B a weight or an intermediate ("Metodologia", first paragraph);
+ *   - for the current input an index set I along the shared contraction
+ *     dimension is picked and only A[:, I] B[I, :] is formed ("Mecanismo
+ *     Central");
+ *   - each contraction index j is scored by the L2 norm of activation column
+ *     j, and the ceil(rho * d) best-scored indices are kept, rho being the
+ *     retention ratio the user sets ("Estrategia de Selecao");
+ *   - the reduction is applied to the hidden dimension of XW projections, the
+ *     feature dimension of QK^T and the token dimension of PV ("Escopo de
+ *     Aplicacao").
+ *
+ * Readings taken where the pages are silent (listed again in the design doc):
+ *   R1 score of slice k in group g = ||A[rows_g, k]||_2 * ||B[k, :]||_2.
+ *      Passing b == NULL gives the pages' activation-only score.
+ *   R2 selection is made per group of consecutive rows; a whole matrix is a
+ *      single group.  The last group may be short.
+ *   R3 k = ceil(r * K), with a snap for decimal r: x = r*K; if x lies within
+ *      1e-9*K of an integer n then k = n, else k = ceil(x); clamp to [1, K].
+ *   R4 equal scores go to the lower index; the keep/drop decision compares the
+ *      scores after one rounding to IEEE binary32, the key precision of the
+ *      GPU select.
+ *   R5 P.V: for query block g the candidate keys are its causal prefix
+ *      k < K_g = min(L, qblock*(g+1)); the score of key k is
+ *      (sum over the block's queries of P[q,k]) * ||V[k,:]||_2; k_g = kk(r, K_g).
+ *   R6 every sum runs in ascending index order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- retained count ("Estrategia de Selecao": k = ceil(rho d)), reading R3 */
+int64_t oracle_kk(double r, int64_t K)
+{
+    if (!(r > 0.0) || !(r <= 1.0) || K < 1)
+        return -1;
+    double x = r * (double)K;
+    double n = nearbyint(x);
+    int64_t kk;
+    if (fabs(x - n) <= 1e-9 * (double)K)
+        kk = (int64_t)n;
+    else
+        kk = (int64_t)ceil(x);
+    if (kk < 1)
+        kk = 1;
+    if (kk > K)
+        kk = K;
+    return kk;
+}
+
+/* ---- L2 norm of every row of B (K x N, row stride ldb), reading R1 */
+void oracle_rownorms(const double *B, int64_t K, int64_t N, int64_t ldb, double *b)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        double s = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double v = B[k * ldb + n];
+            s += v * v;
+        }
+        b[k] = sqrt(s);
+    }
+}
+
+/* ---- L2 norm of every column of a rows x K block of A ("Estrategia de
+ * Selecao": the activation column norm) */
+void oracle_colnorms(const double *A, int64_t rows, int64_t K, int64_t lda, double *a)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        double s = 0.0;
+        for (int64_t m = 0; m < rows; ++m) {
+            double v = A[m * lda + k];
+            s += v * v;
+        }
+        a[k] = sqrt(s);
+    }
+}
+
+/* ---- scores of every slice k for every group g (readings R1, R2).
+ * s64[g*K + k] = a_{g,k} * b_k   (b == NULL: b_k = 1)
+ * s32[g*K + k] = s64 rounded once to binary32. */
+void oracle_scores(const double *A, int64_t M, int64_t K, int64_t lda, const double *b,
+                   int64_t group_rows, double *s64, float *s32)
+{
+    int64_t G = (M + group_rows - 1) / group_rows;
+    double *a = (double *)malloc((size_t)K * sizeof(double));
+    for (int64_t g = 0; g < G; ++g) {
+        int64_t r0 = g * group_rows;
+        int64_t rows = M - r0 < group_rows ? M - r0 : group_rows;
+        oracle_colnorms(A + r0 * lda, rows, K, lda, a);
+        for (int64_t k = 0; k < K; ++k) {
+            double s = a[k] * (b ? b[k] : 1.0);
+            s64[g * K + k] = s;
+            s32[g * K + k] = (float)s;
+        }
+    }
+    free(a);
+}
+
+/* ---- top-k by a full sort (reading R4).  Order: score descending, then
+ * index ascending.  The first kk of that order are kept and returned in
+ * ascending index order. */
+static const float *sort_keys;
+
+static int by_rank(const void *x, const void *y)
+{
+    int32_t i = *(const int32_t *)x, j = *(const int32_t *)y;
+    float si = sort_keys[i], sj = sort_keys[j];
+    if (si > sj)
+        return -1;
+    if (si < sj)
+        return 1;
+    return (i > j) - (i < j);
+}
+
+static int by_index(const void *x, const void *y)
+{
+    int32_t i = *(const int32_t *)x, j = *(const int32_t *)y;
+    return (i > j) - (i < j);
+}
+
+int oracle_topk(const float *s, int64_t K, int64_t kk, int32_t *idx)
+{
+    if (kk < 1 || kk > K)
+        return -1;
+    int32_t *order = (int32_t *)malloc((size_t)K * sizeof(int32_t));
+    for (int64_t k = 0; k < K; ++k)
+        order[k] = (int32_t)k;
+    sort_keys = s;
+    qsort(order, (size_t)K, sizeof(int32_t), by_rank);
+    memcpy(idx, order, (size_t)kk * sizeof(int32_t));
+    qsort(idx, (size_t)kk, sizeof(int32_t), by_index);
+    free(order);
+    return 0;
+}
+
+/* ---- the reduced product ("Mecanismo Central": A[:, I] B[I, :]) for rows
+ * [m0, m1).  Row m belongs to group m / group_rows, whose kept indices are
+ * idx[g*ldidx + 0 .. kk-1].  Outer-product form, ascending j (reading R6).
+ * Y row m is written at Y[(m - m0)*ldy]. */
+void oracle_reduced(const double *A, int64_t lda, const double *B, int64_t ldb, int64_t N,
+                    int64_t group_rows, const int32_t *idx, int64_t ldidx, int64_t kk,
+                    int64_t m0, int64_t m1, double *Y, int64_t ldy)
+{
+    for (int64_t m = m0; m < m1; ++m) {
+        const int32_t *I = idx + (m / group_rows) * ldidx;
+        double *y = Y + (m - m0) * ldy;
+        for (int64_t n = 0; n < N; ++n)
+            y[n] = 0.0;
+        for (int64_t j = 0; j < kk; ++j) {
+            int64_t k = I[j];
+            double a = A[m * lda + k];
+            const double *brow = B + k * ldb;
+            for (int64_t n = 0; n < N; ++n)
+                y[n] += a * brow[n];
+        }
+    }
+}
+
+/* ---- single entries of the reduced product: out[i] = Y[ms[i], ns[i]], the
+ * same sum in the same order as oracle_reduced. */
+void oracle_reduced_entries(const double *A, int64_t lda, const double *B, int64_t ldb,
+                            int64_t group_rows, const int32_t *idx, int64_t ldidx, int64_t kk,
+                            const int64_t *ms, const int64_t *ns, int64_t count, double *out)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        const int32_t *I = idx + (m / group_rows) * ldidx;
+        double y = 0.0;
+        for (int64_t j = 0; j < kk; ++j) {
+            int64_t k = I[j];
+            y += A[m * lda + k] * B[k * ldb + n];
+        }
+        out[i] = y;
+    }
+}
+
+/* ---- error bound of one group: beta = sum over the dropped slices of
+ * ||A[rows_g, k]|| * ||B[k, :]||, i.e. the sum of the dropped unrounded
+ * scores.  By the triangle inequality and ||a b^T||_F = ||a|| ||b|| it bounds
+ * ||A_g B - A_g[:, I] B[I, :]||_F. */
+double oracle_bound(const double *s64, int64_t K, const int32_t *idx, int64_t kk)
+{
+    unsigned char *kept = (unsigned char *)calloc((size_t)K, 1);
+    for (int64_t j = 0; j < kk; ++j)
+        kept[idx[j]] = 1;
+    double beta = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        if (!kept[k])
+            beta += s64[k];
+    free(kept);
+    return beta;
+}
+
+/* ---- P.V ("Escopo de Aplicacao": the token dimension of PV), reading R5.
+ * P is stored key-major: Pt[k*L + q] = P[q, k].  The functions below see one
+ * head and one query block: Ptb[k*ldp + i] = P[q0 + i, k] for i < nq. */
+int64_t oracle_pv_prefix(int64_t L, int64_t qblock, int64_t g, int causal)
+{
+    if (!causal)
+        return L;
+    int64_t e = qblock * (g + 1);
+    return e < L ? e : L;
+}
+
+void oracle_pv_scores(const double *Ptb, int64_t ldp, int64_t nq, const double *V, int64_t D,
+                      int64_t Kg, double *s64, float *s32)
+{
+    for (int64_t k = 0; k < Kg; ++k) {
+        double mass = 0.0;
+        for (int64_t i = 0; i < nq; ++i)
+            mass += Ptb[k * ldp + i];
+        double vv = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            double v = V[k * D + d];
+            vv += v * v;
+        }
+        double s = mass * sqrt(vv);
+        s64[k] = s;
+        s32[k] = (float)s;
+    }
+}
+
+/* O[i*D + d] = sum_j P[q0+i, I_j] V[I_j, d] over the kept keys, ascending j. */
+void oracle_pv_block(const double *Ptb, int64_t ldp, int64_t nq, const double *V, int64_t D,
+                     const int32_t *idx, int64_t kk, double *O)
+{
+    for (int64_t i = 0; i < nq; ++i) {
+        double *o = O + i * D;
+        for (int64_t d = 0; d < D; ++d)
+            o[d] = 0.0;
+        for (int64_t j = 0; j < kk; ++j) {
+            int64_t k = idx[j];
+            double p = Ptb[k * ldp + i];
+            const double *v = V + k * D;
+            for (int64_t d = 0; d < D; ++d)
+                o[d] += p * v[d];
+        }
+    }
+}
+
+/* Bound for one block: sum over dropped keys k < Kg of
+ * ||P[block, k]||_2 * ||V[k, :]||_2 (L2 column norm of P, not its mass). */
+double oracle_pv_bound(const double *Ptb, int64_t ldp, int64_t nq, const double *V, int64_t D,
+                       int64_t Kg, const int32_t *idx, int64_t kk)
+{
+    unsigned char *kept = (unsigned char *)calloc((size_t)Kg, 1);
+    for (int64_t j = 0; j < kk; ++j)
+        kept[idx[j]] = 1;
+    double beta = 0.0;
+    for (int64_t k = 0; k < Kg; ++k) {
+        if (kept[k])
+            continue;
+        double pp = 0.0;
+        for (int64_t i = 0; i < nq; ++i) {
+            double p = Ptb[k * ldp + i];
+            pp += p * p;
+        }
+        double vv = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            double v = V[k * D + d];
+            vv += v * v;
+        }
+        beta += sqrt(pp) * sqrt(vv);
+    }
+    free(kept);
+    return beta;
+}
