@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark of the Reduced Matrix Multiplication hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: score -> select -> gather -> reduced bf16 MFMA GEMM
+(for r = 1 the dense baseline: the same GEMM kernel on A and B in place).  The
+B row norms depend only on the weight and are computed once, before timing.
+
+Default workload: the attention projection, X 2048x4096 bf16 (N(0,1) times
+lognormal channel scales, 1% outlier channels x20) times W 4096x4096 bf16
+(N(0, 0.02)), one selection per 128-token block, r in {0.3, 0.5, 0.7, 1.0}.
+`value` is the retained-K TFLOP/s of the whole step at r = 0.5
+(2*M*kk*N / step time); per-r stage times, GEMM-only TFLOP/s and the speed-ups
+over r = 1.0 are reported beside it.  Other workloads (--workload mlp_down,
+decode, pv4k, pv16k, tiny) use the same contract.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "reduced-GEMM TFLOP/s on retained K + speedup vs r=1.0 dense, per r"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="attn_proj",
+                   choices=["attn_proj", "mlp_down", "decode", "pv4k", "pv16k", "tiny"])
+    p.add_argument("--ratios", type=str, default=None, help="comma-separated r values")
+    p.add_argument("--headline-r", type=float, default=0.5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-groups", type=int, default=None, help="row groups the oracle baseline runs")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ workloads
+class Linear:
+    """X [M,K] times W [K,N] with per-group selection (attn_proj, mlp_down, decode, tiny)."""
+
+    def __init__(self, name, dev):
+        import numpy as np
+        import torch
+        from input_adaptive_reduced_02_amd import rmm, synth
+        self.rmm, self.torch, self.np = rmm, torch, np
+        self.name = name
+        self.M, self.K, self.N = synth.FULL_SHAPES[name]
+        self.gr = synth.GROUP_ROWS[name]
+        self.ratios = synth.RATIOS[name]
+        t0 = time.time()
+        d = synth.linear_inputs(name)
+        self.host = d
+        if d["dtype"] == "bf16":
+            self.A = torch.from_numpy(d["A"].view(np.int16)).view(torch.bfloat16).to(dev)
+            self.B = torch.from_numpy(d["B"].view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            self.A = torch.from_numpy(d["A"]).to(dev)
+            self.B = torch.from_numpy(d["B"]).to(dev)
+        self.f32 = d["dtype"] == "f32"
+        self.bnorm = rmm.rmm_rownorms(self.B)   # once per weight, outside the timed step
+        torch.cuda.synchronize()
+        log(f"[bench] {name}: inputs {self.M}x{self.K} @ {self.K}x{self.N} ready in {time.time() - t0:.1f}s")
+        self.G = -(-self.M // self.gr)
+        self.dev = dev
+
+    def describe(self, r):
+        dt = "fp32" if self.f32 else "bf16"
+        return (f"{self.name}: X {self.M}x{self.K} {dt} @ W {self.K}x{self.N} {dt}, "
+                f"{self.gr}-row selection groups, r={r}")
+
+    def stages(self, r):
+        """[(name, fn)] of one step at ratio r, buffers allocated once here."""
+        rmm, torch = self.rmm, self.torch
+        kk = rmm.rmm_kk(r, self.K)
+        self.kk = kk
+        Y = torch.empty((self.M, self.N), dtype=torch.float32 if self.f32 else torch.bfloat16, device=self.dev)
+        if kk == self.K and not self.f32:
+            return [("gemm", lambda: rmm.rmm_gemm(self.A, self.B, None, kk, self.gr, Y=Y))], kk
+        kpad = rmm.rmm_kk_pad(kk)
+        idx = torch.empty((self.G, kpad), dtype=torch.int32, device=self.dev)
+        Ap = torch.empty((self.M, kpad), dtype=torch.bfloat16, device=self.dev)
+        ws = torch.empty(max(1, rmm.rmm_select_workspace_bytes(self.M, self.K, self.gr)), dtype=torch.uint8,
+                         device=self.dev)
+        sel = ("select", lambda: rmm.rmm_select(self.A, r, self.gr, bnorm=self.bnorm, idx=idx, ws=ws))
+        if self.f32:
+            Bp = torch.empty((kpad, self.N), dtype=torch.bfloat16, device=self.dev)
+            return [sel,
+                    ("gather", lambda: rmm.rmm_gather(self.A, idx, kk, self.gr, Apanel=Ap, B=self.B, Bpanel=Bp)),
+                    ("gemm", lambda: rmm.rmm_gemm(Ap, Bp, None, kk, self.gr, Y=Y))], kk
+        return [sel,
+                ("gather", lambda: rmm.rmm_gather(self.A, idx, kk, self.gr, Apanel=Ap)),
+                ("gemm", lambda: rmm.rmm_gemm(Ap, self.B, idx, kk, self.gr, Y=Y))], kk
+
+    def flops(self, r):
+        return 2.0 * self.M * self.rmm.rmm_kk(r, self.K) * self.N
+
+    def gemm_bytes(self, r):
+        """Algorithmic HBM bytes of one reduced-GEMM launch: kept B rows, the A
+        panel (or A), and Y."""
+        kk = self.rmm.rmm_kk(r, self.K)
+        yb = 4 if self.f32 else 2
+        return 2.0 * kk * self.N + 2.0 * self.M * kk + yb * self.M * self.N
+
+    bound = property(lambda self: "hbm" if self.name == "decode" else "mfma")
+
+    def cpu_baseline(self, r, groups):
+        """The oracle (single-threaded fp64 C) on `groups` row groups at ratio r:
+        scores of those groups, selection, reduced product."""
+        import oracle as O
+        np = self.np
+        d = self.host
+        widen = O.widen_f32 if self.f32 else O.widen_bf16
+        rows = min(self.M, groups * self.gr)
+        A64 = widen(d["A"][:rows])
+        B64 = widen(d["B"])
+        b = O.rownorms(B64)   # per-weight, outside the timed part (as on the GPU)
+        t0 = time.perf_counter()
+        sel = O.select(A64, r, self.gr, b)
+        Y = O.reduced(A64, B64, sel["idx"], sel["kk"], self.gr)
+        dt = time.perf_counter() - t0
+        del Y
+        fl = 2.0 * rows * sel["kk"] * self.N
+        return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
+                    sample=f"{rows // self.gr} of {self.G} row groups ({rows} of {self.M} rows) at r={r}: "
+                           f"score + select + reduced product, {fl / 1e9:.2f} GFLOP in {dt:.1f} s",
+                    seconds=round(dt, 2))
+
+
+class PV:
+    """P.V reduced along keys: 32 heads, head dim 128, 128-query blocks, causal."""
+
+    def __init__(self, L, dev):
+        import torch
+        from input_adaptive_reduced_02_amd import rmm, synth
+        self.rmm, self.torch = rmm, torch
+        self.H, self.L, self.D = 32, L, 128
+        self.name = f"pv{L // 1024}k"
+        self.ratios = synth.RATIOS["pv"]
+        self.dev = dev
+        t0 = time.time()
+        q, k, v = synth.pv_qkv(self.H, L, self.D)
+        self.Pt = synth.pv_probs_t(q, k, causal=True, device=dev)
+        self.V = torch.from_numpy(v.view("int16")).view(torch.bfloat16).to(dev)
+        torch.cuda.synchronize()
+        self.G = L // 128
+        log(f"[bench] {self.name}: P ({self.H}x{L}x{L} bf16, key-major) ready in {time.time() - t0:.1f}s")
+
+    def describe(self, r):
+        return (f"{self.name}: P.V, {self.H} heads, L={self.L}, head dim {self.D}, bf16, causal, "
+                f"128-query blocks, r={r}")
+
+    def _kks(self, r):
+        return [self.rmm.rmm_kk(r, min(self.L, 128 * (g + 1))) for g in range(self.G)]
+
+    def stages(self, r):
+        rmm, torch = self.rmm, self.torch
+        O_ = torch.empty((self.H, self.L, self.D), dtype=torch.bfloat16, device=self.dev)
+        need = rmm.rmm_attn_pv_workspace_bytes(self.H, self.L, self.D, r)
+        ws = torch.empty(max(1, need), dtype=torch.uint8, device=self.dev)
+        self.kk = max(self._kks(r))
+        return [("attn_pv", lambda: rmm.rmm_attn_pv(self.Pt, self.V, r, O=O_, ws=ws))], self.kk
+
+    def flops(self, r):
+        return sum(2.0 * 128 * kk * self.D for kk in self._kks(r)) * self.H
+
+    def gemm_bytes(self, r):
+        kept_p = sum(kk * 128 * 2.0 for kk in self._kks(r)) * self.H
+        return kept_p + 2.0 * 2 * self.H * self.L * self.D   # + V once, + O once
+
+    bound = property(lambda self: "hbm")
+
+    def cpu_baseline(self, r, groups):
+        import numpy as np
+
+        import oracle as O
+        # `groups` (head 0, block) pairs from the end of the sequence (the heaviest)
+        Pt0 = self.Pt[0].cpu().view(torch_int16(self.torch)).numpy().view(np.uint16)
+        V0 = self.V[0].cpu().view(torch_int16(self.torch)).numpy().view(np.uint16)
+        fl = 0.0
+        t0 = time.perf_counter()
+        for g in range(self.G - 1, max(-1, self.G - 1 - groups), -1):
+            sel = O.pv_select_block(Pt0, V0, self.L, 128, g, r, True)
+            O.pv_block(sel["Ptb"], sel["V"], sel["idx"])
+            fl += 2.0 * 128 * sel["kk"] * self.D
+        dt = time.perf_counter() - t0
+        return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
+                    sample=f"{groups} query blocks of head 0 (the last ones) at r={r}: score + select + "
+                           f"reduced P.V, {fl / 1e9:.2f} GFLOP in {dt:.1f} s", seconds=round(dt, 2))
+
+
+def torch_int16(torch):
+    return torch.int16
+
+
+# ------------------------------------------------------------------ timing
+def time_stages(torch, stages, steps, warmup):
+    """Warm up, then time `steps` whole steps (no events inside) and, in a second
+    pass, each stage with events on the launch stream.  Returns (ms_per_step,
+    {stage: mean ms})."""
+    for _ in range(warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(steps):
+        for _, fn in stages:
+            fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        for j, (_, fn) in enumerate(stages):
+            evs[i][j].record(s)
+            fn()
+        evs[i][-1].record(s)
+    torch.cuda.synchronize()
+    per = {}
+    for j, (name, _) in enumerate(stages):
+        per[name] = sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
+    return ms_step, per
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): this build has no "
+              "multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    if args.workload in ("pv4k", "pv16k"):
+        W = PV(4096 if args.workload == "pv4k" else 16384, dev)
+    else:
+        W = Linear(args.workload, dev)
+    ratios = [float(x) for x in args.ratios.split(",")] if args.ratios else list(W.ratios)
+    if 1.0 not in ratios:
+        ratios.append(1.0)
+    headline = args.headline_r if args.headline_r in ratios else ratios[0]
+
+    per_r = {}
+    for r in ratios:
+        stages, kk = W.stages(r)
+        ms_step, per = time_stages(torch, stages, args.steps, args.warmup)
+        gemm_name = stages[-1][0]
+        fl = W.flops(r)
+        per_r[r] = dict(kk=kk, ms_per_step=ms_step, stage_ms=per, step_tflops=fl / (ms_step * 1e-3) / 1e12,
+                        gemm_tflops=fl / (per[gemm_name] * 1e-3) / 1e12,
+                        gemm_gbs=W.gemm_bytes(r) / (per[gemm_name] * 1e-3) / 1e9)
+        log(f"[bench] r={r}: kk={kk} step {ms_step * 1e3:.1f} us, stages "
+            + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in per.items())
+            + f", gemm {per_r[r]['gemm_tflops']:.1f} TFLOP/s {per_r[r]['gemm_gbs']:.0f} GB/s")
+        del stages
+    base = per_r[1.0]
+    gname = "gemm" if "gemm" in base["stage_ms"] else "attn_pv"
+    for r, v in per_r.items():
+        v["speedup_step_vs_r1"] = base["ms_per_step"] / v["ms_per_step"]
+        v["speedup_gemm_vs_r1"] = base["stage_ms"][gname] / v["stage_ms"][gname]
+
+    h = per_r[headline]
+    gemm_ms = h["stage_ms"][gname]
+    if W.bound == "mfma":
+        achieved = W.flops(headline) / (gemm_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None)
+    else:
+        achieved = W.gemm_bytes(headline) / (gemm_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None)
+    roof["kernel"] = gname
+    roof["kernel_ms"] = round(gemm_ms, 5)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        groups = args.cpu_groups
+        if groups is None:
+            groups = {"attn_proj": 4, "mlp_down": 1, "decode": 1, "tiny": 1, "pv4k": 8, "pv16k": 2}[W.name]
+        log(f"[bench] oracle baseline on {groups} groups ...")
+        cpu = W.cpu_baseline(headline, groups)
+        log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s ({cpu['seconds']} s)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(h["step_tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded stand-in for the pages' model activations and weights)",
+        "config": {"workload": W.describe(headline), "r": headline, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_r": {str(r): {k: (round(x, 5) if isinstance(x, float) else
+                               ({kk: round(vv, 5) for kk, vv in x.items()} if isinstance(x, dict) else x))
+                           for k, x in v.items()} for r, v in per_r.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

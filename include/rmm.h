@@ -1,0 +1,188 @@
+/*
+ * rmm.h -- C ABI of librmm.so: the hot path of Reduced Matrix Multiplication
+ * (RMM) on AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Reduced Matrix Multiplication: Input-Adaptive Matrix-Product
+ * Reduction for LLM Inference" (Lan, Li, Zhou).  Its technical summary
+ * (gist.science, section "Metodologia") writes each Transformer matmul as
+ * Y = A B, scores every index of the shared contraction dimension from the
+ * current input, keeps the ceil(rho d) best and forms only A[:, I] B[I, :];
+ * it applies this to XW projections, to QK^T and to P V along the token
+ * dimension ("Escopo de Aplicacao").  The authors' abstract (arXiv
+ * 2608.13426) states the reduction keeps model weights unmodified and needs no
+ * training.
+ *
+ * Readings of this library where the pages are silent:
+ *   - score of slice k in a group of rows = ||A[rows, k]||_2 * ||B[k, :]||_2;
+ *     with no B norms it is the pages' activation-only score ||A[rows, k]||_2;
+ *   - one selection per group of `group_rows` consecutive rows (the last group
+ *     may be short); a whole matrix is one group when group_rows >= M;
+ *   - kk = rmm_kk(r, K) (ceil(r*K) for decimal r, see below);
+ *   - equal scores go to the lower index;
+ *   - scores are accumulated in binary64 in ascending row order and rounded
+ *     once to binary32, which is the precision of the keep/drop decision;
+ *   - P.V: per query block g the candidate keys are the causal prefix
+ *     k < min(L, qblock*(g+1)); score = block column mass of P * ||V[k, :]||_2.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *     allocates and frees nothing; scratch memory comes from a caller-owned
+ *     workspace sized by the *_workspace_bytes functions.
+ *   - Matrices are row-major with explicit leading dimensions in elements.
+ *   - Every device pointer is 16-byte aligned, and every leading dimension is
+ *     a multiple of 8 (bf16) or 4 (fp32) elements: rows start 16-byte aligned.
+ *     A matrix with leading dimension ld is readable for rows*ld elements.
+ *   - bf16 tensors are passed as their 16-bit patterns (uint16_t).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; no entry point synchronises the host.
+ *   - Return value: RMM_OK, or RMM_EINVAL (bad argument, detected on the host
+ *     before anything is enqueued), RMM_EUNSUPPORTED (valid but outside what
+ *     the kernels handle, also before anything is enqueued) or RMM_EHIP (the
+ *     HIP runtime reported an error when enqueueing).
+ *   - Inputs are assumed finite.  Entry points are re-entrant and stateless;
+ *     calls on different streams that share no output buffer may overlap.
+ */
+#ifndef RMM_H
+#define RMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RMM_OK 0
+#define RMM_EINVAL (-1)
+#define RMM_EUNSUPPORTED (-2)
+#define RMM_EHIP (-3)
+
+#define RMM_F32 0
+#define RMM_BF16 1
+
+/* Column padding of panels and index rows: kk is rounded up to this. */
+#define RMM_KPAD 64
+
+/* Retained count: the number of contraction slices kept out of K at
+ * retention ratio r ("Metodologia" > "Estrategia de Selecao": keep
+ * ceil(rho d)).  r is read as the decimal the user meant: with x = r*K in
+ * binary64, if x is within 1e-9*K of an integer n the result is n, else
+ * ceil(x); the result is clamped to [1, K].  Returns -1 when r is not in
+ * (0, 1] (NaN included) or K < 1.  Pure host function. */
+int64_t rmm_kk(double r, int64_t K);
+
+/* kk rounded up to a multiple of RMM_KPAD (the width of panels and index
+ * rows).  Returns -1 for kk < 1. */
+int64_t rmm_kk_pad(int64_t kk);
+
+/* Static text of a status code. */
+const char *rmm_strerror(int status);
+
+/* B row norms: bnorm[k] = ||B[k, :]||_2 for k < K, summed in binary64 in
+ * ascending column order.  This is the weight factor of the score; it depends
+ * only on B, so callers compute it once per weight and pass it to every
+ * rmm_select call (B itself is never modified).
+ *   B      [K][ldb] of type dt (RMM_BF16 or RMM_F32), device
+ *   bnorm  [K] binary64, device, written
+ * Errors: RMM_EINVAL for NULL pointers, K < 1, N < 1, ldb < N, misalignment. */
+int rmm_rownorms(const void *B, int dt, int64_t K, int64_t N, int64_t ldb, double *bnorm,
+                 void *stream);
+
+/* Workspace bytes rmm_select needs: room for the [G][K] binary32 scores when
+ * the caller passes no `scores` buffer (G = ceil(M / group_rows)), plus K
+ * binary64 row norms when it passes B instead of bnorm.  Returns 0 when the
+ * caller supplies both or needs neither. */
+size_t rmm_select_workspace_bytes(int64_t M, int64_t K, int64_t group_rows, int have_scores,
+                                  int norms_from_B);
+
+/* Score and select ("Estrategia de Selecao").  For every group g of
+ * group_rows consecutive rows of A:
+ *     s[g][k] = binary32( ||A[rows_g, k]||_2 * b_k )
+ * with b_k = bnorm[k] if bnorm != NULL; else the row norms of B computed now
+ * (a full read of B) if B != NULL; else 1 (the pages' activation-only rule).
+ * Then the kk = rmm_kk(r, K) best slices under the order (score descending,
+ * index ascending) are written to idx[g*ldidx + 0 .. kk-1] in ascending
+ * order; entries kk .. rmm_kk_pad(kk)-1 repeat the last kept index.
+ *   A       [M][lda] of type dt, device
+ *   bnorm   [K] binary64 or NULL; B [K][ldb] of type dt or NULL (N columns)
+ *   idx     [G][ldidx] int32, ldidx >= rmm_kk_pad(kk), ldidx % 4 == 0
+ *   scores  [G][K] binary32 or NULL (then held in the workspace)
+ *   thresh  [G] binary32 or NULL: the kk-th best score of each group
+ *   bound   [G] binary64 or NULL: sum of the dropped scores of each group, an
+ *           upper bound of ||A_g B - A_g[:, I] B[I, :]||_F (triangle
+ *           inequality, ||a b^T||_F = ||a|| ||b||) when b is the B norms
+ *   ws      rmm_select_workspace_bytes(...) bytes, device (NULL if 0)
+ * Errors: RMM_EINVAL for bad pointers, sizes, r or a short workspace;
+ * RMM_EUNSUPPORTED for K > 32768. */
+int rmm_select(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm,
+               const void *B, int64_t N, int64_t ldb, double r, int64_t group_rows,
+               int32_t *idx, int64_t ldidx, float *scores, float *thresh, double *bound,
+               void *ws, size_t ws_bytes, void *stream);
+
+/* Gather ("Mecanismo Central": the columns A[:, I] of the reduced product)
+ * into a contiguous bf16 panel:
+ *   Apanel[m][j] = bf16(A[m][idx[g*ldidx + j]])  for j < kk, g = m / group_rows
+ *   Apanel[m][j] = 0                             for kk <= j < rmm_kk_pad(kk)
+ * for rows m < M (binary32 A is rounded to nearest-even bf16).  When Bpanel is
+ * not NULL (only with a single group, G == 1) the kept rows of B are packed
+ * too: Bpanel[j][:] = bf16(B[idx[j]][:]) for j < kk, zero rows after that.
+ *   A       [M][lda] of type dt; idx [G][ldidx] int32 (ldidx >= kk)
+ *   Apanel  [M][ldp] bf16, ldp >= rmm_kk_pad(kk)
+ *   B       [K][ldb] of type dt (N columns, N % 8 == 0) or NULL
+ *   Bpanel  [rmm_kk_pad(kk)][ldbp] bf16 or NULL, ldbp >= N
+ * Errors: RMM_EINVAL for bad pointers/sizes, or Bpanel with more than one group. */
+int rmm_gather(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const int32_t *idx,
+               int64_t ldidx, int64_t kk, int64_t group_rows, uint16_t *Apanel, int64_t ldp,
+               const void *B, int64_t N, int64_t ldb, uint16_t *Bpanel, int64_t ldbp,
+               void *stream);
+
+/* Workspace bytes rmm_gemm needs (currently 0 for every shape). */
+size_t rmm_gemm_workspace_bytes(int64_t M, int64_t N, int64_t kk, int64_t group_rows);
+
+/* The reduced product ("Mecanismo Central"), bf16 inputs, fp32 accumulation:
+ *   Y[m][n] = sum_{j < kk} A[m][j] * B[row(g, j)][n],   g = m / group_rows,
+ *   row(g, j) = idx[g*ldidx + j] if idx != NULL, else j.
+ * With idx the kept rows of B are read in place (no B panel); A is the
+ * gathered panel.  With idx == NULL, A and B are read as they are: this is
+ * the dense product when kk == K (the r = 1 baseline, same kernels), or the
+ * product of an A panel with a packed B panel.  Accumulation is ascending in
+ * j within each 64-wide slab of a tile, so results are deterministic.
+ *   A    [M][lda] bf16, lda >= kk
+ *   B    bf16 rows of length N (N % 8 == 0) with leading dimension ldb
+ *   idx  [G][ldidx] int32 or NULL, ldidx >= kk, ldidx % 4 == 0
+ *   Y    [M][ldy] of type ydt (RMM_BF16: rounded to nearest-even; RMM_F32)
+ * Errors: RMM_EINVAL for bad pointers/sizes. */
+int rmm_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, const int32_t *idx,
+             int64_t ldidx, int64_t M, int64_t N, int64_t kk, int64_t group_rows, void *Y,
+             int ydt, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes rmm_attn_pv needs for H heads of length L: per-key V norms,
+ * the [H][G][L] block scores (unless scores_out is given) and the kept-key
+ * lists (unless idx_out is given), G = ceil(L / qblock).  r == 1 needs none. */
+size_t rmm_attn_pv_workspace_bytes(int64_t H, int64_t L, int64_t D, double r, int64_t qblock,
+                                   int causal, int have_idx_out, int have_scores_out);
+
+/* P.V reduced along the key (token) dimension ("Escopo de Aplicacao": PV,
+ * token dimension).  For head h and query block g (queries
+ * q0 = g*qblock .. min(L, q0+qblock)-1), with candidate keys k < K_g
+ * (K_g = min(L, qblock*(g+1)) if causal, else L):
+ *   score[h][g][k] = binary32( (sum_{q in block} P[h][q][k]) * ||V[h][k][:]||_2 )
+ *   I = the kk_g = rmm_kk(r, K_g) best keys (ties to the lower index)
+ *   O[h][q][:] = sum_{k in I} P[h][q][k] * V[h][k][:]
+ * r == 1 skips scoring and selection: the dense causal product, same kernel.
+ *   Pt   [H][L][L] bf16, KEY-MAJOR: Pt[h][k][q] = P[h][q][k]
+ *   V    [H][L][D] bf16;  O [H][L][D] of type odt
+ *   idx_out    [H*G][ldidx_out] int32 or NULL: kept keys, ascending, padded
+ *              by repeating the last one up to rmm_kk_pad(kk_g)
+ *   scores_out [H][G][L] binary32 or NULL (entries k >= K_g untouched)
+ * Supported: D == 128, qblock == 128, L % 8 == 0, L <= 32768, else
+ * RMM_EUNSUPPORTED.  Errors: RMM_EINVAL for bad pointers/sizes/r/workspace. */
+int rmm_attn_pv(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D, double r,
+                int64_t qblock, int causal, void *O, int odt, int32_t *idx_out,
+                int64_t ldidx_out, float *scores_out, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMM_H */

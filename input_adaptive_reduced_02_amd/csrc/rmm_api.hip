@@ -1,0 +1,218 @@
+// rmm_api.hip -- the extern "C" entry points of librmm.so (include/rmm.h).
+//
+// Host code only: argument validation (every RMM_EINVAL / RMM_EUNSUPPORTED is
+// decided before anything is enqueued), workspace carving, and kernel
+// launches on the caller's stream.  No allocation, no host synchronisation.
+#include "../../include/rmm.h"
+#include "rmm_internal.h"
+
+#include <cmath>
+
+using namespace rmm;
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned8(const void *p) { return ((uintptr_t)p & 7u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+int elem_size(int dt) { return dt == RMM_BF16 ? 2 : dt == RMM_F32 ? 4 : 0; }
+
+// a [rows][ld] matrix of type dt: non-NULL, 16-byte aligned, rows 16-byte aligned
+bool ok_matrix(const void *p, int dt, int64_t cols, int64_t ld)
+{
+    const int es = elem_size(dt);
+    if (!p || es == 0 || cols < 1 || ld < cols) return false;
+    return aligned16(p) && (ld * es) % 16 == 0;
+}
+
+hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RMM_OK : RMM_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t rmm_kk(double r, int64_t K)
+{
+    if (!(r > 0.0) || !(r <= 1.0) || K < 1) return -1;
+    return kk_rule(r, K);
+}
+
+int64_t rmm_kk_pad(int64_t kk) { return kk < 1 ? -1 : pad_up(kk); }
+
+const char *rmm_strerror(int status)
+{
+    switch (status) {
+    case RMM_OK: return "success";
+    case RMM_EINVAL: return "invalid argument";
+    case RMM_EUNSUPPORTED: return "unsupported shape or type";
+    case RMM_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int rmm_rownorms(const void *B, int dt, int64_t K, int64_t N, int64_t ldb, double *bnorm, void *stream)
+{
+    if (K < 1 || !ok_matrix(B, dt, N, ldb) || !bnorm || !aligned8(bnorm)) return RMM_EINVAL;
+    return hip_status(launch_rownorms(B, dt, K, N, ldb, bnorm, as_stream(stream)));
+}
+
+size_t rmm_select_workspace_bytes(int64_t M, int64_t K, int64_t group_rows, int have_scores,
+                                  int norms_from_B)
+{
+    if (M < 1 || K < 1 || group_rows < 1) return 0;
+    const int64_t G = (M + group_rows - 1) / group_rows;
+    size_t n = 0;
+    if (!have_scores) n += align_up((size_t)G * (size_t)K * sizeof(float));
+    if (norms_from_B) n += align_up((size_t)K * sizeof(double));
+    return n;
+}
+
+int rmm_select(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm,
+               const void *B, int64_t N, int64_t ldb, double r, int64_t group_rows, int32_t *idx,
+               int64_t ldidx, float *scores, float *thresh, double *bound, void *ws,
+               size_t ws_bytes, void *stream)
+{
+    if (M < 1 || K < 1 || group_rows < 1 || !ok_matrix(A, dt, K, lda)) return RMM_EINVAL;
+    const int64_t kk = rmm_kk(r, K);
+    if (kk < 1) return RMM_EINVAL;
+    if (!idx || !aligned16(idx) || ldidx < pad_up(kk) || ldidx % 4 != 0) return RMM_EINVAL;
+    if (bnorm && !aligned8(bnorm)) return RMM_EINVAL;
+    const bool from_B = !bnorm && B;
+    if (from_B && !ok_matrix(B, dt, N, ldb)) return RMM_EINVAL;
+    if (scores && !aligned4(scores)) return RMM_EINVAL;
+    if (thresh && !aligned4(thresh)) return RMM_EINVAL;
+    if (bound && !aligned8(bound)) return RMM_EINVAL;
+    const size_t need = rmm_select_workspace_bytes(M, K, group_rows, scores != nullptr, from_B);
+    if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
+    if (K > kSelectMaxK) return RMM_EUNSUPPORTED;
+
+    hipStream_t s = as_stream(stream);
+    const int64_t G = (M + group_rows - 1) / group_rows;
+    char *w = (char *)ws;
+    float *sc = scores;
+    if (!sc) {
+        sc = (float *)w;
+        w += align_up((size_t)G * K * sizeof(float));
+    }
+    const double *bn = bnorm;
+    if (from_B) {
+        double *tmp = (double *)w;
+        if (hipError_t e = launch_rownorms(B, dt, K, N, ldb, tmp, s)) return hip_status(e);
+        bn = tmp;
+    }
+    if (hipError_t e = launch_colscore(A, dt, M, K, lda, bn, group_rows, sc, s)) return hip_status(e);
+    SelectShape sh{};
+    sh.groups = G;
+    sh.K = K;
+    sh.lds = K;
+    sh.kk = kk;
+    sh.pv = 0;
+    return hip_status(launch_select(sc, sh, idx, ldidx, thresh, bound, s));
+}
+
+int rmm_gather(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const int32_t *idx,
+               int64_t ldidx, int64_t kk, int64_t group_rows, uint16_t *Apanel, int64_t ldp,
+               const void *B, int64_t N, int64_t ldb, uint16_t *Bpanel, int64_t ldbp, void *stream)
+{
+    if (M < 1 || K < 1 || group_rows < 1 || !ok_matrix(A, dt, K, lda)) return RMM_EINVAL;
+    if (kk < 1 || kk > K) return RMM_EINVAL;
+    if (!idx || !aligned16(idx) || ldidx < kk || ldidx % 4 != 0) return RMM_EINVAL;
+    const int64_t kpad = pad_up(kk);
+    if (!ok_matrix(Apanel, RMM_BF16, kpad, ldp)) return RMM_EINVAL;
+    if (Bpanel) {
+        if ((M + group_rows - 1) / group_rows != 1) return RMM_EINVAL;
+        if (!ok_matrix(B, dt, N, ldb) || N % 8 != 0) return RMM_EINVAL;
+        if (!ok_matrix(Bpanel, RMM_BF16, N, ldbp)) return RMM_EINVAL;
+    }
+    return hip_status(launch_gather(A, dt, M, lda, idx, ldidx, kk, group_rows, Apanel, ldp, B, N, ldb,
+                                    Bpanel, ldbp, as_stream(stream)));
+}
+
+size_t rmm_gemm_workspace_bytes(int64_t, int64_t, int64_t, int64_t) { return 0; }
+
+int rmm_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, const int32_t *idx,
+             int64_t ldidx, int64_t M, int64_t N, int64_t kk, int64_t group_rows, void *Y, int ydt,
+             int64_t ldy, void *ws, size_t ws_bytes, void *stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    if (M < 1 || N < 1 || kk < 1 || group_rows < 1) return RMM_EINVAL;
+    if (!ok_matrix(A, RMM_BF16, kk, lda)) return RMM_EINVAL;
+    if (!ok_matrix(B, RMM_BF16, N, ldb) || N % 8 != 0) return RMM_EINVAL;
+    if (idx && (!aligned16(idx) || ldidx < kk || ldidx % 4 != 0)) return RMM_EINVAL;
+    if (!ok_matrix(Y, ydt, N, ldy)) return RMM_EINVAL;
+    if (kk > INT32_MAX || (M + group_rows - 1) / group_rows > INT32_MAX / 64) return RMM_EUNSUPPORTED;
+    return hip_status(launch_gemm(A, lda, B, ldb, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy,
+                                  as_stream(stream)));
+}
+
+size_t rmm_attn_pv_workspace_bytes(int64_t H, int64_t L, int64_t D, double r, int64_t qblock,
+                                   int causal, int have_idx_out, int have_scores_out)
+{
+    (void)causal;
+    if (H < 1 || L < 1 || D < 1 || qblock < 1) return 0;
+    if (!(r > 0.0) || !(r < 1.0)) return 0;  // r == 1 (or invalid): no scoring, no selection
+    const int64_t G = (L + qblock - 1) / qblock;
+    size_t n = align_up((size_t)H * L * sizeof(double));
+    if (!have_scores_out) n += align_up((size_t)H * G * L * sizeof(float));
+    if (!have_idx_out) n += align_up((size_t)H * G * pad_up(L) * sizeof(int32_t));
+    return n;
+}
+
+int rmm_attn_pv(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D, double r,
+                int64_t qblock, int causal, void *O, int odt, int32_t *idx_out, int64_t ldidx_out,
+                float *scores_out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (H < 1 || L < 1 || D < 1 || qblock < 1) return RMM_EINVAL;
+    if (!Pt || !V || !aligned16(Pt) || !aligned16(V)) return RMM_EINVAL;
+    if (!(r > 0.0) || !(r <= 1.0)) return RMM_EINVAL;
+    if (!O || elem_size(odt) == 0 || !aligned16(O)) return RMM_EINVAL;
+    if (scores_out && !aligned4(scores_out)) return RMM_EINVAL;
+    const int64_t G = (L + qblock - 1) / qblock;
+    if (idx_out && (!aligned16(idx_out) || ldidx_out % 4 != 0 || ldidx_out < pad_up(L)))
+        return RMM_EINVAL;
+    if (D != 128 || qblock != 128 || L % 8 != 0 || L > kSelectMaxK) return RMM_EUNSUPPORTED;
+    const bool dense = r >= 1.0;
+    const size_t need = rmm_attn_pv_workspace_bytes(H, L, D, r, qblock, causal, idx_out != nullptr,
+                                                    scores_out != nullptr);
+    if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
+
+    hipStream_t s = as_stream(stream);
+    if (dense)
+        return hip_status(launch_pv_gemm(Pt, V, H, L, qblock, causal, 1.0, nullptr, 0, O, odt, s));
+    char *w = (char *)ws;
+    double *vnorm = (double *)w;
+    w += align_up((size_t)H * L * sizeof(double));
+    float *sc = scores_out;
+    if (!sc) {
+        sc = (float *)w;
+        w += align_up((size_t)H * G * L * sizeof(float));
+    }
+    int32_t *ix = idx_out;
+    int64_t ldix = ldidx_out;
+    if (!ix) {
+        ix = (int32_t *)w;
+        ldix = pad_up(L);
+    }
+    if (hipError_t e = launch_pv_score(Pt, V, H, L, D, qblock, causal, vnorm, sc, s)) return hip_status(e);
+    SelectShape sh{};
+    sh.groups = H * G;
+    sh.K = L;
+    sh.lds = L;
+    sh.pv = 1;
+    sh.Gq = G;
+    sh.qblock = qblock;
+    sh.causal = causal;
+    sh.r = r;
+    if (hipError_t e = launch_select(sc, sh, ix, ldix, nullptr, nullptr, s)) return hip_status(e);
+    return hip_status(launch_pv_gemm(Pt, V, H, L, qblock, causal, r, ix, ldix, O, odt, s));
+}
+
+}  // extern "C"

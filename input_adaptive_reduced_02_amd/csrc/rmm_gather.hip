@@ -1,0 +1,108 @@
+// rmm_gather.hip -- compaction of the kept slices into bf16 panels (gfx950).
+//
+// Forms the columns A[:, I] of the reduced product A[:, I] B[I, :]
+// ("Reduced Matrix Multiplication..." technical summary, Metodologia >
+// Mecanismo Central) as a dense, zero-padded bf16 panel the GEMM streams with
+// plain 16-byte loads.  Optionally packs the kept rows B[I, :] as well (single
+// group only; the GEMM otherwise reads kept B rows in place by index).
+//
+// HBM-bound data movement.  Each thread produces 8 consecutive panel columns
+// of one row (one 16-byte store) from 8 ascending kept indices, so a wave's
+// loads of A fall within one row and its stores are fully coalesced.
+#include "rmm_internal.h"
+
+namespace rmm {
+
+template <int DT>
+__global__ void __launch_bounds__(256)
+k_gather_a(const void *__restrict__ Av, int64_t M, int64_t lda, const int32_t *__restrict__ idx,
+           int64_t ldidx, int64_t kk, int64_t gr, uint16_t *__restrict__ Ap, int64_t ldp,
+           int64_t chunks_per_row)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t m = t / chunks_per_row;
+    const int64_t j0 = (t % chunks_per_row) * 8;
+    if (m >= M) return;
+    const int32_t *I = idx + (m / gr) * ldidx;
+    uint32_t h[8];
+    if (j0 + 8 <= kk) {
+        const int4 i0 = *(const int4 *)(I + j0);
+        const int4 i1 = *(const int4 *)(I + j0 + 4);
+        const int32_t ks[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+        if (DT == 1) {
+            const uint16_t *row = (const uint16_t *)Av + m * lda;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = row[ks[e]];
+        } else {
+            const float *row = (const float *)Av + m * lda;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16(row[ks[e]]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t j = j0 + e;
+            h[e] = 0;
+            if (j < kk) {
+                const int32_t k = I[j];
+                if (DT == 1)
+                    h[e] = ((const uint16_t *)Av)[m * lda + k];
+                else
+                    h[e] = f32_to_bf16(((const float *)Av)[m * lda + k]);
+            }
+        }
+    }
+    uint4 o = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    *(uint4 *)(Ap + m * ldp + j0) = o;
+}
+
+// Bp[j][:] = bf16(B[idx[j]][:]) for j < kk, zero for kk <= j < kpad.
+template <int DT>
+__global__ void __launch_bounds__(256)
+k_gather_b(const void *__restrict__ Bv, int64_t N, int64_t ldb, const int32_t *__restrict__ idx,
+           int64_t kk, int64_t kpad, uint16_t *__restrict__ Bp, int64_t ldbp, int64_t chunks_per_row)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t j = t / chunks_per_row;
+    const int64_t n0 = (t % chunks_per_row) * 8;
+    if (j >= kpad) return;
+    uint4 o = make_uint4(0, 0, 0, 0);
+    if (j < kk) {
+        const int64_t k = idx[j];
+        if (DT == 1) {
+            o = *(const uint4 *)((const uint16_t *)Bv + k * ldb + n0);
+        } else {
+            const float *row = (const float *)Bv + k * ldb + n0;
+            const float4 a = *(const float4 *)row, b = *(const float4 *)(row + 4);
+            o = make_uint4(f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16), f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16),
+                           f32_to_bf16(b.x) | (f32_to_bf16(b.y) << 16), f32_to_bf16(b.z) | (f32_to_bf16(b.w) << 16));
+        }
+    }
+    *(uint4 *)(Bp + j * ldbp + n0) = o;
+}
+
+hipError_t launch_gather(const void *A, int dt, int64_t M, int64_t lda, const int32_t *idx,
+                         int64_t ldidx, int64_t kk, int64_t group_rows, uint16_t *Ap, int64_t ldp,
+                         const void *B, int64_t N, int64_t ldb, uint16_t *Bp, int64_t ldbp,
+                         hipStream_t s)
+{
+    const int64_t kpad = pad_up(kk);
+    const int64_t cpr = kpad / 8;
+    const int64_t threads = M * cpr;
+    dim3 grid((unsigned)((threads + 255) / 256));
+    if (dt == 1)
+        hipLaunchKernelGGL(k_gather_a<1>, grid, dim3(256), 0, s, A, M, lda, idx, ldidx, kk, group_rows, Ap, ldp, cpr);
+    else
+        hipLaunchKernelGGL(k_gather_a<0>, grid, dim3(256), 0, s, A, M, lda, idx, ldidx, kk, group_rows, Ap, ldp, cpr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !Bp) return e;
+    const int64_t cb = N / 8;
+    dim3 gb((unsigned)((kpad * cb + 255) / 256));
+    if (dt == 1)
+        hipLaunchKernelGGL(k_gather_b<1>, gb, dim3(256), 0, s, B, N, ldb, idx, kk, kpad, Bp, ldbp, cb);
+    else
+        hipLaunchKernelGGL(k_gather_b<0>, gb, dim3(256), 0, s, B, N, ldb, idx, kk, kpad, Bp, ldbp, cb);
+    return hipGetLastError();
+}
+
+}  // namespace rmm

@@ -145,7 +145,7 @@ def topk(s32, kk_, lib=None):
     return out
 
 
-def _near_ties(s64_row, s32_row, idx):
+def near_ties(s64_row, s32_row, idx):
     """Indices whose unrounded score lies within NEAR_TIE_REL of the k-th score."""
     kept32 = s32_row[idx]
     last = idx[kept32 == kept32.min()].max()  # the kk-th element of the rank order
@@ -177,7 +177,7 @@ def select(A, r, group_rows, b=None, lib=None):
         thresh[g] = s32[g][idx[g]].min()
         row = np.ascontiguousarray(s64[g])
         bound[g] = lib.oracle_bound(_p(row, _D), K, _p(idx[g], _I32), kk_)
-        near.append(_near_ties(s64[g], s32[g], idx[g]))
+        near.append(near_ties(s64[g], s32[g], idx[g]))
     return dict(kk=kk_, idx=idx, s64=s64, s32=s32, thresh=thresh, bound=bound, near=near)
 
 
@@ -284,11 +284,11 @@ def pv_select_block(Pt, V, L, qblock, g, r, causal=True, lib=None):
     kk_ = kk(r, Kg, lib)
     idx = topk(s32, kk_, lib)
     return dict(Kg=Kg, kk=kk_, idx=idx, s64=s64, s32=s32, Ptb=Ptb, V=Vg,
-                near=_near_ties(s64, s32, idx))
+                near=near_ties(s64, s32, idx))
 
 
 __all__ = [
     "load", "widen_bf16", "widen_f32", "kk", "rownorms", "colnorms", "scores", "topk", "select",
     "reduced", "reduced_entries", "dense", "bound", "pv_prefix", "pv_block_inputs", "pv_scores",
-    "pv_block", "pv_bound", "pv_select_block", "NEAR_TIE_REL",
+    "pv_block", "pv_bound", "pv_select_block", "near_ties", "NEAR_TIE_REL",
 ]

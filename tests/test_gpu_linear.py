@@ -1,0 +1,238 @@
+"""GPU parity of the linear-layer hot path (score -> select -> gather -> reduced
+GEMM, and the r = 1 dense baseline) against the oracle, through the C ABI.
+
+Small cases span several tiles and ragged tails (short last group, N not a
+multiple of the tile, kk not a multiple of 8 or 64) and are compared element by
+element; the full workload sizes are compared on every group's scores and kept
+set and on sampled output rows.  Scores, B norms, kept sets and panels must be
+bit-exact (both sides sum in binary64 in ascending order and round once to
+binary32); outputs within the bound documented in tests/gpu_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import DEV, check_output, compare_sets, down, log, up_bf16, up_f32, widen
+from input_adaptive_reduced_02_amd import rmm, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def make_case(workload, M, K, N, seed=0):
+    d = synth.linear_inputs(workload, M, K, N, seed=seed)
+    if d["dtype"] == "bf16":
+        A64, B64 = O.widen_bf16(d["A"]), O.widen_bf16(d["B"])
+        A, B = up_bf16(d["A"]), up_bf16(d["B"])
+    else:
+        A64, B64 = O.widen_f32(d["A"]), O.widen_f32(d["B"])
+        A, B = up_f32(d["A"]), up_f32(d["B"])
+    return dict(A=A, B=B, A64=A64, B64=B64, f32=d["dtype"] == "f32", raw=d)
+
+
+def run_chain(c, r, gr, bnorm):
+    """The hot path through the C ABI; returns (idx, scores, thresh, bound, Ap, Y)."""
+    A, B = c["A"], c["B"]
+    M, K = A.shape
+    kk = rmm.rmm_kk(r, K)
+    G = -(-M // gr)
+    scores = torch.empty((G, K), dtype=torch.float32, device=DEV)
+    thresh = torch.empty(G, dtype=torch.float32, device=DEV)
+    bound = torch.empty(G, dtype=torch.float64, device=DEV)
+    idx = torch.zeros((G, rmm.rmm_kk_pad(kk)), dtype=torch.int32, device=DEV)
+    rmm.rmm_select(A, r, gr, bnorm=bnorm, idx=idx, scores=scores, thresh=thresh, bound=bound)
+    check_index_range(idx, K)
+    if c["f32"]:
+        Ap, Bp = rmm.rmm_gather(A, idx, kk, gr, B=B)
+        Y = rmm.rmm_gemm(Ap, Bp, None, kk, gr, ydt=torch.float32)
+    else:
+        Ap, _ = rmm.rmm_gather(A, idx, kk, gr)
+        Y = rmm.rmm_gemm(Ap, B, idx, kk, gr)
+    torch.cuda.synchronize()
+    return idx, scores, thresh, bound, Ap, Y
+
+
+def check_index_range(idx, K):
+    """Host check before any kernel reads rows by these indices."""
+    torch.cuda.synchronize()
+    ig = down(idx)
+    assert ig.min() >= 0 and ig.max() < K, f"kept index out of range [{ig.min()}, {ig.max()}], K={K}"
+
+
+def check_selection(c, r, gr, bnorm, idx, scores, thresh, bound, tag):
+    sel = O.select(c["A64"], r, gr, O.rownorms(c["B64"]))
+    kk = sel["kk"]
+    assert np.array_equal(down(scores), sel["s32"]), f"{tag}: scores differ from the oracle"
+    ig = down(idx)
+    exact = True
+    for g in range(ig.shape[0]):
+        exact &= compare_sets(ig[g], sel, g, kk, tag)
+        assert np.all(ig[g, kk:] == ig[g, kk - 1]), f"{tag}: padding of group {g}"
+    if exact:
+        assert np.array_equal(down(thresh), sel["thresh"])
+    assert np.allclose(down(bound), sel["bound"], rtol=1e-6, atol=0)
+    n_near = sum(len(x) for x in sel["near"])
+    log(f"  {tag}: kk={kk} groups={ig.shape[0]} sets exact={exact} near-tie indices={n_near}")
+    return sel, ig
+
+
+SMALL = [
+    # (workload, M, K, N, group_rows, r)
+    ("tiny", 64, 256, 128, 64, 0.5),                 # the full tiny workload
+    ("attn_proj", 300, 1000, 264, 128, 0.3),         # groups 128,128,44; N tail 8; kk=300
+    ("attn_proj", 300, 1000, 264, 128, 0.5),
+    ("mlp_down", 256, 2048, 512, 128, 0.7),
+    ("decode", 64, 4096, 1024, 64, 0.3),             # narrow tiles, kk=1229
+    ("attn_proj", 200, 520, 72, 128, 0.37),          # kk=193: not a multiple of 8
+    ("mlp_down", 96, 136, 40, 32, 0.9),              # group_rows 32, kk=123
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-g{c[4]}-r{c[5]}")
+def test_chain_small(case):
+    workload, M, K, N, gr, r = case
+    tag = f"{workload} {M}x{K}x{N} gr={gr} r={r}"
+    log(f"case {tag}")
+    c = make_case(workload, M, K, N)
+    bnorm = rmm.rmm_rownorms(c["B"])
+    torch.cuda.synchronize()
+    b_ref = O.rownorms(c["B64"])
+    assert np.array_equal(down(bnorm), b_ref), "B row norms differ from the oracle"
+    idx, scores, thresh, bound, Ap, Y = run_chain(c, r, gr, bnorm)
+    sel, ig = check_selection(c, r, gr, bnorm, idx, scores, thresh, bound, tag)
+    kk = sel["kk"]
+    # panel: exact bf16 of the kept columns, zero padding
+    ap = down(Ap)
+    A_bits = c["raw"]["A"]
+    for m in range(M):
+        cols = ig[m // gr, :kk]
+        if c["f32"]:
+            want = torch.from_numpy(np.ascontiguousarray(A_bits[m, cols])).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        else:
+            want = A_bits[m, cols]
+        assert np.array_equal(ap[m, :kk], want), f"panel row {m}"
+        assert np.all(ap[m, kk:] == 0)
+    # output, computed by the oracle on the GPU's kept sets
+    Yref = O.reduced(c["A64"], c["B64"], ig, kk, gr)
+    Sabs = O.reduced(np.abs(c["A64"]), np.abs(c["B64"]), ig, kk, gr)
+    check_output(widen(Y), Yref, Sabs, kk, tag, f32_inputs=c["f32"])
+
+
+@pytest.mark.parametrize("shape", [(300, 1000, 264, 128), (64, 4096, 1024, 64), (200, 520, 72, 128),
+                                   (130, 64, 8, 128)])
+def test_dense_baseline_small(shape):
+    """r = 1: the same GEMM kernel, A and B read in place, equals the oracle's dense product."""
+    M, K, N, gr = shape
+    c = make_case("attn_proj", M, K, N, seed=3)
+    log(f"dense {shape}")
+    Y = rmm.rmm_gemm(c["A"], c["B"], None, K, gr)
+    Y32 = rmm.rmm_gemm(c["A"], c["B"], None, K, gr, ydt=torch.float32)
+    torch.cuda.synchronize()
+    Yref = O.dense(c["A64"], c["B64"])
+    Sabs = O.dense(np.abs(c["A64"]), np.abs(c["B64"]))
+    check_output(widen(Y), Yref, Sabs, K, f"dense bf16 {shape}")
+    # fp32 output: no output rounding, only accumulation error
+    err = np.abs(widen(Y32) - Yref)
+    assert np.all(err <= 1.01 * K * 2.0 ** -24 * Sabs + 1e-30)
+
+
+def test_determinism():
+    c = make_case("attn_proj", 512, 2048, 1024)
+    bnorm = rmm.rmm_rownorms(c["B"])
+    out1 = run_chain(c, 0.5, 128, bnorm)
+    out2 = run_chain(c, 0.5, 128, bnorm)
+    for a, b in zip(out1, out2):
+        assert torch.equal(a, b)
+
+
+def test_edge_cases():
+    # all-zero columns and columns of equal norm: ties everywhere, lower index wins
+    rng = np.random.default_rng(5)
+    M, K, N, gr = 128, 512, 256, 64
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    a[:, 100:300] = 0.0                    # 200 zero columns (score 0)
+    a[:, 300:400] = a[:, 7:8]              # 100 copies of column 7 (equal scores)
+    b = np.full((K, N), 0.5, np.float32)   # equal B row norms
+    A = up_bf16(synth.f32_to_bf16_bits(a))
+    B = up_bf16(synth.f32_to_bf16_bits(b))
+    A64, B64 = widen(A), widen(B)
+    bnorm = rmm.rmm_rownorms(B)
+    for r in (1e-6, 0.05, 0.2, 0.4, 0.5, 0.9, 1.0):
+        idx = torch.zeros((M // gr, rmm.rmm_kk_pad(rmm.rmm_kk(r, K))), dtype=torch.int32, device=DEV)
+        rmm.rmm_select(A, r, gr, bnorm=bnorm, idx=idx)
+        check_index_range(idx, K)
+        sel = O.select(A64, r, gr, O.rownorms(B64))
+        ig = down(idx)
+        assert np.array_equal(ig[:, :sel["kk"]], sel["idx"]), r
+        kk = sel["kk"]
+        Ap, _ = rmm.rmm_gather(A, idx, kk, gr)
+        Y = rmm.rmm_gemm(Ap, B, idx, kk, gr)
+        torch.cuda.synchronize()
+        Yref = O.reduced(A64, B64, ig, kk, gr)
+        check_output(widen(Y), Yref, O.reduced(np.abs(A64), B64, ig, kk, gr), kk, f"ties r={r}")
+    # kk = 1, K tiny, a group larger than M, one-row groups, the activation-only rule
+    for (M, K, N, gr, r, act) in [(64, 8, 8, 64, 0.1, False), (50, 64, 16, 1000, 0.5, False),
+                                  (16, 96, 24, 1, 0.25, False), (160, 256, 64, 128, 0.5, True)]:
+        c = make_case("attn_proj", M, K, N, seed=9)
+        bn = None if act else rmm.rmm_rownorms(c["B"])
+        idx = torch.zeros((-(-M // gr), rmm.rmm_kk_pad(rmm.rmm_kk(r, K))), dtype=torch.int32, device=DEV)
+        rmm.rmm_select(c["A"], r, gr, bnorm=bn, idx=idx)
+        check_index_range(idx, K)
+        Y = rmm.linear(c["A"], c["B"], r, gr, bnorm=bn, activation_only=act)
+        torch.cuda.synchronize()
+        sel = O.select(c["A64"], r, gr, None if act else O.rownorms(c["B64"]))
+        ig = down(idx)
+        assert np.array_equal(ig[:, :sel["kk"]], sel["idx"])
+        Yref = O.reduced(c["A64"], c["B64"], sel["idx"], sel["kk"], gr)
+        Sabs = O.reduced(np.abs(c["A64"]), np.abs(c["B64"]), sel["idx"], sel["kk"], gr)
+        check_output(widen(Y), Yref, Sabs, sel["kk"], f"edge M={M} K={K} N={N} gr={gr} r={r} act={act}")
+
+
+# ---------------------------------------------------------------- full sizes
+FULL = [("attn_proj", 0.3), ("attn_proj", 0.5), ("attn_proj", 0.7), ("attn_proj", 1.0),
+        ("mlp_down", 0.5), ("mlp_down", 0.7), ("mlp_down", 0.9), ("mlp_down", 1.0),
+        ("decode", 0.3), ("decode", 0.5), ("decode", 0.7), ("decode", 1.0)]
+
+_full_cache = {}
+
+
+def _full(workload):
+    if workload not in _full_cache:
+        _full_cache.clear()
+        M, K, N = synth.FULL_SHAPES[workload]
+        c = make_case(workload, M, K, N)
+        c["bnorm"] = rmm.rmm_rownorms(c["B"])
+        c["b_ref"] = O.rownorms(c["B64"])
+        c["A64abs"] = np.abs(c["A64"])
+        c["B64abs"] = np.abs(c["B64"])
+        _full_cache[workload] = c
+    return _full_cache[workload]
+
+
+@pytest.mark.parametrize("workload,r", FULL, ids=lambda x: str(x))
+def test_full_size(workload, r):
+    """Full workload shape, in the launch configuration the benchmark times:
+    every group's scores and kept set exact; sampled rows element by element."""
+    c = _full(workload)
+    M, K = c["A"].shape
+    N = c["B"].shape[1]
+    gr = synth.GROUP_ROWS[workload]
+    tag = f"{workload} {M}x{K}x{N} r={r}"
+    log(f"full {tag}")
+    assert np.array_equal(down(c["bnorm"]), c["b_ref"])
+    rng = np.random.default_rng(11)
+    G = -(-M // gr)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, G)]))
+    if r == 1.0:
+        Y = rmm.linear(c["A"], c["B"], r, gr, bnorm=c["bnorm"])
+        torch.cuda.synchronize()
+        ig = np.arange(K, dtype=np.int32)[None, :].repeat(G, 0)
+        kk = K
+    else:
+        idx, scores, thresh, bound, Ap, Y = run_chain(c, r, gr, c["bnorm"])
+        sel, ig = check_selection(c, r, gr, c["bnorm"], idx, scores, thresh, bound, tag)
+        kk = sel["kk"]
+    Yg = widen(Y)
+    Yref = np.stack([O.reduced(c["A64"], c["B64"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
+    Sabs = np.stack([O.reduced(c["A64abs"], c["B64abs"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
+    check_output(Yg[rows], Yref, Sabs, kk, tag + f" ({len(rows)} rows)")
