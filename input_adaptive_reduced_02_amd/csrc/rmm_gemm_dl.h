@@ -1,0 +1,242 @@
+// rmm_gemm_dl.h -- prefill-shape reduced GEMM with a global->LDS DMA pipeline
+// (gfx950).  Included by rmm_gemm.hip.
+//
+// Same product as k_gemm (Y[rows_g, :] = Apanel[rows_g, 0:kk] * B[I_g, :]),
+// organised the way gfx950 wants it:
+//   * operands go from global memory straight into LDS with 16-byte
+//     global_load_lds_dwordx4 DMA loads (lane l of a wave writes bytes
+//     [16l, 16l+16) of a 1 KiB LDS block): no VGPR staging and no VALU work on
+//     the load path, so a 3-deep ring of 64-deep slabs is in flight;
+//   * the A tile is kept k-contiguous (an MFMA A fragment is one
+//     ds_read_b128); the B tile stays n-contiguous as in memory and the MFMA
+//     B fragments come from ds_read_b64_tr_b16, whose 16-lane blocks return a
+//     4(k) x 16(n) sub-block transposed (lane i of the block gets column i,
+//     four consecutive k);
+//   * the kept-row index list is DMA-loaded into a small per-wave LDS ring one
+//     slab ahead of the B loads that use it, so dropped rows of B are never
+//     fetched and no load result ever waits in a register.
+// The DMA loads are issued from inline assembly (they have no register
+// outputs) and every wait is an explicit s_waitcnt whose count follows from
+// the fixed issue order, so the compiler's conservative LDS-DMA alias waits
+// never serialise the ring.
+// Bank-conflict-free layouts come from choosing, per lane, which 16-byte
+// global chunk it fetches: A row r stores chunk c at slot c ^ swz(r); B row k
+// stores chunk c at slot c ^ 2*(k & 3) (the four rows one transposed read
+// touches then land on four distinct 32-byte bank groups).
+//
+// Tile 128 x 256 x 64, 4 waves of 64 x 128, v_mfma_f32_32x32x16_bf16.
+#pragma once
+#include "rmm_tile.h"
+
+namespace rmm {
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+struct DlShape {
+    static constexpr int TM = 128, TN = 256, BK = 64, WM = 64, WN = 128, FM = 2, FN = 4;
+    static constexpr int NSTAGE = 3;
+    static constexpr int A_ELEMS = TM * BK;          // 16 KiB
+    static constexpr int B_ELEMS = BK * TN;          // 32 KiB
+    static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
+    static constexpr int A_LOADS = A_ELEMS * 2 / 1024 / 4;   // 1 KiB DMA blocks per wave per slab: 4
+    static constexpr int B_LOADS = B_ELEMS * 2 / 1024 / 4;   // 8
+    static constexpr int IDX_RING = 4;                       // slabs of indices per wave
+};
+
+__device__ __forceinline__ int swz_bt(int k) { return 2 * (k & 3); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// DMA: every lane copies 16 (or 4) bytes from its global address to
+// LDS[m0 + 16*lane] (or 4*lane).  m0 is the wave-uniform LDS base.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+#define RMM_VMWAIT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
+
+template <bool IDX>
+__global__ void __launch_bounds__(256)
+k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
+          const int32_t *__restrict__ idx, int64_t ldidx, int64_t M, int64_t N, int64_t kk, int64_t gr,
+          void *__restrict__ Y, int ydt, int64_t ldy, int tiles_per_group, int m_tiles, int n_tiles)
+{
+    using S = DlShape;
+    constexpr int TM = S::TM, TN = S::TN, BK = S::BK, WM = S::WM, WN = S::WN, FM = S::FM, FN = S::FN;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[S::NSTAGE * S::STAGE_ELEMS];
+    __shared__ __attribute__((aligned(256))) int32_t iring[4][S::IDX_RING][BK];
+
+    const int total = m_tiles * n_tiles;
+    const int per = (total + 7) / 8;
+    const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (t >= total) return;
+    const int nt = t / m_tiles, mt = t % m_tiles;
+    const int64_t g = mt / tiles_per_group;
+    const int64_t row0 = g * gr + (int64_t)(mt % tiles_per_group) * TM;
+    const int64_t row_end = (g * gr + gr < M) ? g * gr + gr : M;
+    const int64_t col0 = (int64_t)nt * TN;
+    const int32_t *I = IDX ? idx + g * ldidx : nullptr;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5;              // which of the two B rows of a DMA block
+    const int nkt = (int)((kk + BK - 1) / BK);
+
+    // ---- per-lane global sources of the DMA loads (slab offsets added per slab)
+    const uint16_t *a_src[S::A_LOADS];
+#pragma unroll
+    for (int i = 0; i < S::A_LOADS; ++i) {
+        const int r = (wave * S::A_LOADS + i) * 8 + (lane >> 3);
+        int64_t row = row0 + r;
+        if (row > M - 1) row = M - 1;
+        a_src[i] = A + row * lda + (((lane & 7) ^ swz(r)) << 3);
+    }
+    const uint16_t *b_src[S::B_LOADS];
+#pragma unroll
+    for (int i = 0; i < S::B_LOADS; ++i) {
+        const int k = (wave * S::B_LOADS + i) * 2 + h;
+        int64_t c = col0 + (((lane & 31) ^ swz_bt(k)) << 3);
+        b_src[i] = B + ((c < N) ? c : 0);   // columns past N: any valid chunk, never stored
+    }
+    const uint32_t smem0 = lds_addr(smem);
+    const uint32_t iring0 = lds_addr(&iring[wave][0][0]);
+
+    // index entries of slab kt into ring slot kt % 4 (slabs past the end
+    // re-read slab 0, always in bounds and never used)
+    auto issue_idx = [&](int kt) {
+        if constexpr (IDX) {
+            const int64_t j = (int64_t)(kt < nkt ? kt : 0) * BK + lane;
+            dma4(I + j, iring0 + (kt % S::IDX_RING) * BK * 4);
+        }
+    };
+    // the A and B tiles of slab kt into ring stage kt % 3
+    auto issue_ab = [&](int kt) {
+        const int64_t kbase = (int64_t)kt * BK;
+        const uint32_t sa = smem0 + (kt % S::NSTAGE) * S::STAGE_ELEMS * 2;
+        const uint32_t sb = sa + S::A_ELEMS * 2;
+#pragma unroll
+        for (int i = 0; i < S::A_LOADS; ++i) dma16(a_src[i] + kbase, sa + (wave * S::A_LOADS + i) * 1024);
+#pragma unroll
+        for (int i = 0; i < S::B_LOADS; ++i) {
+            const int jr = wave * 16 + 2 * i + h;          // row of the slab
+            int64_t krow;
+            if constexpr (IDX) krow = iring[wave][kt % S::IDX_RING][jr];
+            else krow = kbase + jr;
+            if (kbase + jr >= kk) krow = 0;                // past kk: row 0 (A is zero there)
+            dma16(b_src[i] + krow * ldb, sb + (wave * S::B_LOADS + i) * 1024);
+        }
+    };
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.0f;
+
+    // per-lane byte offsets of the transposed B reads within a stage's B tile
+    const int blk = lane >> 4, li = lane & 15, s_ = li >> 2, q = li & 3;
+    int b_off[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const int nb = wn * WN + fn * 32 + (blk & 1) * 16;
+        const int c = (nb >> 3) + (q >> 1);
+        const int k = (blk >> 1) * 8 + s_;
+        b_off[fn] = k * TN * 2 + ((c ^ swz_bt(k)) << 4) + (q & 1) * 8;
+    }
+
+    // ---- prologue.  Issue order of this wave's loads is always
+    //   ..., IDX(kt+1), AB(kt), IDX(kt+2), AB(kt+1), ...
+    // (IDX only with an index list).  AB is 12 loads, IDX one.
+    issue_idx(0);
+    issue_idx(1);
+    RMM_VMWAIT(0);
+    issue_ab(0);
+    issue_idx(2);
+    if (nkt > 1) issue_ab(1);
+
+    for (int kt = 0; kt < nkt; ++kt) {
+        // slab kt must be in LDS; IDX(kt+2) and AB(kt+1) may stay in flight
+        if constexpr (IDX) {
+            if (kt + 1 < nkt) RMM_VMWAIT(13); else RMM_VMWAIT(1);
+        } else {
+            if (kt + 1 < nkt) RMM_VMWAIT(12); else RMM_VMWAIT(0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // every wave's slab kt landed, and stage (kt+2)%3 (slab kt-1) is free
+        if (kt + 2 < nkt) {
+            if constexpr (IDX) {
+                // IDX(kt+2) done; only AB(kt+1) may remain
+                RMM_VMWAIT(12);
+            }
+            issue_idx(kt + 3);
+            issue_ab(kt + 2);
+        } else {
+            issue_idx(kt + 3);   // keeps the per-iteration issue order uniform
+        }
+        uint16_t *sa = smem + (kt % S::NSTAGE) * S::STAGE_ELEMS;
+        const char *sb = (const char *)(sa + S::A_ELEMS);
+        if ((int64_t)(kt + 1) * BK > kk) {
+            // partial last slab: clear A columns >= kk (B rows there are row 0, finite)
+            for (int e = threadIdx.x; e < TM * BK; e += 256) {
+                const int r = e / BK, col = e % BK;
+                const int c = col >> 3, pos = ((c ^ swz(r)) << 3) + (col & 7);
+                if ((int64_t)kt * BK + col >= kk) sa[r * BK + pos] = 0;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int c = 2 * ks + (lane >> 5);
+            bf16x8 af[FM], bfr[FN];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int r = wm * WM + fm * 32 + (lane & 31);
+                af[fm] = *(const bf16x8 *)(sa + r * BK + ((c ^ swz(r)) << 3));
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const char *p = sb + b_off[fn] + ks * 16 * TN * 2;
+                shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p));
+                shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p + 4 * TN * 2));
+                bfr[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+        }
+    }
+    RMM_VMWAIT(0);   // the trailing index loads
+
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int64_t col = col0 + wn * WN + fn * 32 + acc_col(lane);
+            if (col >= N) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = row0 + wm * WM + fm * 32 + acc_row(lane, v);
+                if (row >= row_end) continue;
+                if (ydt == 1)
+                    ((uint16_t *)Y)[row * ldy + col] = (uint16_t)f32_to_bf16(acc[fm][fn][v]);
+                else
+                    ((float *)Y)[row * ldy + col] = acc[fm][fn][v];
+            }
+        }
+    }
+}
+
+}  // namespace rmm

@@ -10,38 +10,22 @@
 // the keys of the contiguous index range [t*kpt, (t+1)*kpt) in registers.
 //   1. Threshold T = the kk-th largest key, found bit by bit from the top, two
 //      bits per round: the three candidate prefixes are counted at once with
-//      per-thread compares, a wavefront shuffle reduction and one LDS
-//      exchange between the 16 waves (16 rounds, one barrier each).
-//   2. Ordered compaction: one block-wide exclusive scan of the per-thread
-//      counts of keys > T and == T gives every thread its output position;
-//      keys == T are kept in index order until kk is reached.
+//      wavefront ballots and scalar popcounts, then summed over the 16 waves
+//      through LDS (16 rounds, one barrier each).
+//   2. Ordered compaction: per-wave exclusive counts of keys > T and == T come
+//      from ballots masked to the lower lanes (mbcnt), per-wave totals from one
+//      LDS exchange; every thread then knows its output position, and keys
+//      == T are kept in index order until kk is reached.
 // No atomics anywhere, so the output is deterministic.
 #include "rmm_internal.h"
 
 namespace rmm {
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
+// Sum of a wave-uniform value over the workgroup's 16 waves; every thread
+// gets the result.  `slot` is one of two alternating LDS rows, so consecutive
+// calls need a single barrier each.
+__device__ __forceinline__ uint64_t block_sum_uniform(uint64_t v, uint64_t *slot)
 {
-    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    lo = __shfl_xor(lo, m, 64);
-    hi = __shfl_xor(hi, m, 64);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d)
-{
-    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    lo = __shfl_up(lo, d, 64);
-    hi = __shfl_up(hi, d, 64);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Sum over the workgroup; every thread gets the result.  `slot` is one of two
-// alternating LDS rows, so consecutive calls need a single barrier each.
-__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t *slot)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_u64(v, m);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) slot[wave] = v;
     __syncthreads();
@@ -90,15 +74,15 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     int round = 0;
     for (int sh2 = 29; sh2 >= 1; sh2 -= 2, ++round) {
         const int32_t c1 = T | (1 << sh2), c2 = T | (2 << sh2), c3 = T | (3 << sh2);
-        uint32_t n1 = 0, n2 = 0, n3 = 0;
+        uint32_t n1 = 0, n2 = 0, n3 = 0;   // wave-uniform counts
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            n1 += key[i] >= c1;
-            n2 += key[i] >= c2;
-            n3 += key[i] >= c3;
+            n1 += __popcll(__ballot(key[i] >= c1));
+            n2 += __popcll(__ballot(key[i] >= c2));
+            n3 += __popcll(__ballot(key[i] >= c3));
         }
-        const uint64_t tot = block_sum_u64((uint64_t)n1 | ((uint64_t)n2 << 21) | ((uint64_t)n3 << 42),
-                                           red[round & 1]);
+        const uint64_t tot = block_sum_uniform((uint64_t)n1 | ((uint64_t)n2 << 21) | ((uint64_t)n3 << 42),
+                                               red[round & 1]);
         const int64_t t1 = tot & 0x1fffff, t2 = (tot >> 21) & 0x1fffff, t3 = tot >> 42;
         const int v = (t3 >= kk) ? 3 : (t2 >= kk) ? 2 : (t1 >= kk) ? 1 : 0;
         T |= v << sh2;
@@ -107,26 +91,23 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         const int32_t c1 = T | 1;
         uint32_t n1 = 0;
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) n1 += key[i] >= c1;
-        const uint64_t tot = block_sum_u64(n1, red[round & 1]);
+        for (int i = 0; i < KPT; ++i) n1 += __popcll(__ballot(key[i] >= c1));
+        const uint64_t tot = block_sum_uniform(n1, red[round & 1]);
         if ((int64_t)tot >= kk) T = c1;
     }
 
     // ---- 2. ordered compaction
-    uint32_t gt = 0, eq = 0;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes < this one
+    uint32_t gt_w = 0, eq_w = 0, gt_tot_w = 0, eq_tot_w = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        gt += key[i] > T;
-        eq += key[i] == T;
+        const uint64_t bg = __ballot(key[i] > T), be = __ballot(key[i] == T);
+        gt_w += __popcll(bg & below);
+        eq_w += __popcll(be & below);
+        gt_tot_w += __popcll(bg);
+        eq_tot_w += __popcll(be);
     }
-    const uint64_t mine = ((uint64_t)gt << 32) | eq;
-    uint64_t incl = mine;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint64_t o = shfl_up_u64(incl, d);
-        if (lane >= d) incl += o;
-    }
-    if (lane == 63) wsum[wave] = incl;
+    if (lane == 0) wsum[wave] = ((uint64_t)gt_tot_w << 32) | eq_tot_w;
     __syncthreads();
     uint64_t before = 0, total = 0;
 #pragma unroll
@@ -135,8 +116,8 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         before += (w < wave) ? x : 0;
         total += x;
     }
-    const uint64_t excl = before + incl - mine;
-    const int64_t gt_before = (int64_t)(excl >> 32), eq_before = (int64_t)(excl & 0xffffffffu);
+    const int64_t gt_before = (int64_t)(before >> 32) + gt_w;
+    const int64_t eq_before = (int64_t)(before & 0xffffffffu) + eq_w;
     const int64_t need_eq = kk - (int64_t)(total >> 32);  // >= 1 by the choice of T
     int64_t pos = gt_before + (eq_before < need_eq ? eq_before : need_eq);
     int64_t eq_seen = eq_before;
