@@ -28,30 +28,32 @@ SOURCES = ["rmm_api.hip", "rmm_score.hip", "rmm_select.hip", "rmm_gather.hip", "
            "rmm_pv.hip"]
 
 
-def _compile(src):
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, objdir=OBJ, extra=(), csrc=CSRC):
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(csrc, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj, r.stderr
 
 
-def build(verbose=False):
-    """Compile every HIP source and link librmm.so; returns the library path."""
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose=False, out=LIB, extra=(), objdir=OBJ, csrc=CSRC):
+    """Compile every HIP source and link librmm.so (or `out`, with `extra`
+    compiler flags, sources from `csrc` and objects in `objdir`); returns the
+    library path."""
+    os.makedirs(objdir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda src: _compile(src, objdir, extra, csrc), SOURCES))
     for _, err in results:
         if verbose and err.strip():
             print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for o, _ in results], "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -21,10 +21,9 @@
 // never serialise the ring.
 // Bank-conflict-free layouts come from choosing, per lane, which 16-byte
 // global chunk it fetches: A row r stores chunk c at slot c ^ swz(r); B row k
-// stores chunk c at slot c ^ 2*(k & 3) (the four rows one transposed read
-// touches then land on four distinct 32-byte bank groups).
+// stores chunk c at slot c ^ swz_bt(k) (see below).
 //
-// Tile 128 x 256 x 64, 4 waves of 64 x 128, v_mfma_f32_32x32x16_bf16.
+// Tile 128 x 256 x 64, v_mfma_f32_32x32x16_bf16.
 #pragma once
 #include "rmm_tile.h"
 
@@ -33,18 +32,30 @@ namespace rmm {
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
+// NW = 4: waves 2 x 2 of 64 x 128;  NW = 8: waves 2 x 4 of 64 x 64 (two waves
+// per SIMD, so one can feed the matrix core while the other waits on LDS).
+template <int NW>
 struct DlShape {
-    static constexpr int TM = 128, TN = 256, BK = 64, WM = 64, WN = 128, FM = 2, FN = 4;
+    static constexpr int TM = 128, TN = 256, BK = 64;
+    static constexpr int WAVES_M = 2, WAVES_N = NW / 2;
+    static constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N, FM = WM / 32, FN = WN / 32;
     static constexpr int NSTAGE = 3;
     static constexpr int A_ELEMS = TM * BK;          // 16 KiB
     static constexpr int B_ELEMS = BK * TN;          // 32 KiB
     static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
-    static constexpr int A_LOADS = A_ELEMS * 2 / 1024 / 4;   // 1 KiB DMA blocks per wave per slab: 4
-    static constexpr int B_LOADS = B_ELEMS * 2 / 1024 / 4;   // 8
+    static constexpr int A_LOADS = A_ELEMS * 2 / 1024 / NW;  // 1 KiB DMA blocks per wave per slab
+    static constexpr int B_LOADS = B_ELEMS * 2 / 1024 / NW;
     static constexpr int IDX_RING = 4;                       // slabs of indices per wave
 };
 
-__device__ __forceinline__ int swz_bt(int k) { return 2 * (k & 3); }
+// B row k stores 16-byte chunk c at slot c ^ swz_bt(k).  The XOR values
+// {0, 6, 10, 12} make the 4 rows x 2 chunks one 16-lane block of a transposed
+// read touches distinct modulo 8 slots (32 banks), and the 4 rows x 4 chunks
+// of two blocks distinct modulo 16 slots (64 banks).
+__device__ __forceinline__ int swz_bt(int k) { return (0xcA60 >> (4 * (k & 3))) & 0xf; }
+
+template <int N>
+__device__ __forceinline__ void vmwait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
@@ -61,18 +72,19 @@ __device__ __forceinline__ void dma4(const void *g, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
-#define RMM_VMWAIT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
 
-template <bool IDX>
-__global__ void __launch_bounds__(256)
+template <int NW, bool IDX>
+__global__ void __launch_bounds__(64 * NW)
 k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
           const int32_t *__restrict__ idx, int64_t ldidx, int64_t M, int64_t N, int64_t kk, int64_t gr,
           void *__restrict__ Y, int ydt, int64_t ldy, int tiles_per_group, int m_tiles, int n_tiles)
 {
-    using S = DlShape;
+    using S = DlShape<NW>;
     constexpr int TM = S::TM, TN = S::TN, BK = S::BK, WM = S::WM, WN = S::WN, FM = S::FM, FN = S::FN;
+    constexpr int AB = S::A_LOADS + S::B_LOADS;   // DMA loads per wave per slab
+    constexpr int NT = 64 * NW;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[S::NSTAGE * S::STAGE_ELEMS];
-    __shared__ __attribute__((aligned(256))) int32_t iring[4][S::IDX_RING][BK];
+    __shared__ __attribute__((aligned(256))) int32_t iring[NW][S::IDX_RING][BK];
 
     const int total = m_tiles * n_tiles;
     const int per = (total + 7) / 8;
@@ -87,7 +99,7 @@ k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
     const int h = lane >> 5;              // which of the two B rows of a DMA block
     const int nkt = (int)((kk + BK - 1) / BK);
 
@@ -127,7 +139,7 @@ k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
         for (int i = 0; i < S::A_LOADS; ++i) dma16(a_src[i] + kbase, sa + (wave * S::A_LOADS + i) * 1024);
 #pragma unroll
         for (int i = 0; i < S::B_LOADS; ++i) {
-            const int jr = wave * 16 + 2 * i + h;          // row of the slab
+            const int jr = (wave * S::B_LOADS + i) * 2 + h;  // row of the slab
             int64_t krow;
             if constexpr (IDX) krow = iring[wave][kt % S::IDX_RING][jr];
             else krow = kbase + jr;
@@ -155,40 +167,35 @@ k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
         b_off[fn] = k * TN * 2 + ((c ^ swz_bt(k)) << 4) + (q & 1) * 8;
     }
 
-    // ---- prologue.  Issue order of this wave's loads is always
-    //   ..., IDX(kt+1), AB(kt), IDX(kt+2), AB(kt+1), ...
-    // (IDX only with an index list).  AB is 12 loads, IDX one.
+    // ---- prologue.  Iteration j issues IDX(j+4) then AB(j+2), so this wave's
+    // loads are always ordered ..., IDX(kt+2), AB(kt), IDX(kt+3), AB(kt+1), ...
+    // (IDX only with an index list; AB is A_LOADS + B_LOADS loads, IDX one):
+    // when AB(kt) has landed, the index slab AB(kt+2) needs landed before it.
     issue_idx(0);
     issue_idx(1);
-    RMM_VMWAIT(0);
-    issue_ab(0);
+    vmwait<0>();
     issue_idx(2);
+    issue_ab(0);
+    issue_idx(3);
     if (nkt > 1) issue_ab(1);
 
     for (int kt = 0; kt < nkt; ++kt) {
-        // slab kt must be in LDS; IDX(kt+2) and AB(kt+1) may stay in flight
+        // slab kt must be in LDS; IDX(kt+3) and AB(kt+1) may stay in flight
         if constexpr (IDX) {
-            if (kt + 1 < nkt) RMM_VMWAIT(13); else RMM_VMWAIT(1);
+            if (kt + 1 < nkt) vmwait<AB + 1>(); else vmwait<1>();
         } else {
-            if (kt + 1 < nkt) RMM_VMWAIT(12); else RMM_VMWAIT(0);
+            if (kt + 1 < nkt) vmwait<AB>(); else vmwait<0>();
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // every wave's slab kt landed, and stage (kt+2)%3 (slab kt-1) is free
-        if (kt + 2 < nkt) {
-            if constexpr (IDX) {
-                // IDX(kt+2) done; only AB(kt+1) may remain
-                RMM_VMWAIT(12);
-            }
-            issue_idx(kt + 3);
-            issue_ab(kt + 2);
-        } else {
-            issue_idx(kt + 3);   // keeps the per-iteration issue order uniform
-        }
+        // every wave's slab kt landed, and stage (kt+2)%3 (slab kt-1) is free;
+        // index slot (kt+4)%4 held slab kt's indices, used two iterations ago
+        issue_idx(kt + 4);
+        if (kt + 2 < nkt) issue_ab(kt + 2);
         uint16_t *sa = smem + (kt % S::NSTAGE) * S::STAGE_ELEMS;
         const char *sb = (const char *)(sa + S::A_ELEMS);
         if ((int64_t)(kt + 1) * BK > kk) {
             // partial last slab: clear A columns >= kk (B rows there are row 0, finite)
-            for (int e = threadIdx.x; e < TM * BK; e += 256) {
+            for (int e = threadIdx.x; e < TM * BK; e += NT) {
                 const int r = e / BK, col = e % BK;
                 const int c = col >> 3, pos = ((c ^ swz(r)) << 3) + (col & 7);
                 if ((int64_t)kt * BK + col >= kk) sa[r * BK + pos] = 0;
@@ -218,7 +225,7 @@ k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
                     acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
         }
     }
-    RMM_VMWAIT(0);   // the trailing index loads
+    vmwait<0>();   // the trailing index loads
 
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {

@@ -5,25 +5,39 @@
 // keep the top ceil(rho d) scores), ties going to the lower index, and writes
 // the kept indices in ascending order.
 //
-// One 1024-thread workgroup per group.  Scores are non-negative binary32, so
-// their bit patterns, read as int32, order like the values.  Thread t holds
-// the keys of the contiguous index range [t*kpt, (t+1)*kpt) in registers.
-//   1. Threshold T = the kk-th largest key, found bit by bit from the top, two
-//      bits per round: the three candidate prefixes are counted at once with
-//      wavefront ballots and scalar popcounts, then summed over the 16 waves
-//      through LDS (16 rounds, one barrier each).
-//   2. Ordered compaction: per-wave exclusive counts of keys > T and == T come
-//      from ballots masked to the lower lanes (mbcnt), per-wave totals from one
-//      LDS exchange; every thread then knows its output position, and keys
-//      == T are kept in index order until kk is reached.
-// No atomics anywhere, so the output is deterministic.
+// One 1024-thread workgroup per group; thread t holds the keys of the
+// contiguous index range [t*kpt, (t+1)*kpt) in registers.  Scores are
+// non-negative binary32, so their bit patterns, read as int32, order like the
+// values.  The threshold T (the kk-th largest key) is found in two steps:
+//   1. Value-range histogram: with mn, mx the group's smallest and largest
+//      score, key v goes to bucket floor((v - mn) * 2048 / (mx - mn)), clamped
+//      to 2047.  Subtraction, multiplication by a positive constant and
+//      truncation are monotone in IEEE arithmetic, so the bucket index never
+//      decreases as v grows and equal keys share a bucket: the kk-th largest
+//      key lies in the bucket where the count from the top reaches kk.  Scores
+//      of a smooth distribution spread over many buckets, so the LDS atomics
+//      rarely collide and that bucket holds few keys.
+//   2. The bucket's keys are copied to LDS and T is found among them bit by
+//      bit, two bits per round (three candidate prefixes counted with
+//      wavefront ballots).  Up to 1024 candidates one wave does this alone,
+//      with the candidates in registers and no barriers, starting below the
+//      high bits its smallest and largest candidate share (T lies between
+//      them); beyond that all 16 waves share the search through LDS.
+// Then the ordered compaction: per-wave exclusive counts of keys > T and == T
+// come from ballots masked to the lower lanes, per-wave totals from one LDS
+// exchange; keys == T are kept in index order until kk.  No atomics decide an
+// order and no floating-point sum decides anything, so the output is
+// deterministic.
 #include "rmm_internal.h"
 
 namespace rmm {
 
-// Sum of a wave-uniform value over the workgroup's 16 waves; every thread
-// gets the result.  `slot` is one of two alternating LDS rows, so consecutive
-// calls need a single barrier each.
+constexpr int kBuckets = 2048;
+constexpr int kNW = kSelectThreads / 64;
+
+// Sum of a wave-uniform value over the workgroup's waves; every thread gets
+// the result.  `slot` is one of two alternating LDS rows, so consecutive calls
+// need a single barrier each.
 __device__ __forceinline__ uint64_t block_sum_uniform(uint64_t v, uint64_t *slot)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -31,8 +45,52 @@ __device__ __forceinline__ uint64_t block_sum_uniform(uint64_t v, uint64_t *slot
     __syncthreads();
     uint64_t s = 0;
 #pragma unroll
-    for (int w = 0; w < kSelectThreads / 64; ++w) s += slot[w];
+    for (int w = 0; w < kNW; ++w) s += slot[w];
     return s;
+}
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
+
+// Exclusive prefix sum of a per-thread value v < 2^16 over the workgroup
+// (thread order), plus the total.  Uses ballots on the bits of v.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wtot, uint32_t &total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t below = lanes_below(lane);
+    uint32_t mine = 0, wsum = 0;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+        const uint64_t m = __ballot((v >> b) & 1u);
+        mine += (uint32_t)__popcll(m & below) << b;
+        wsum += (uint32_t)__popcll(m) << b;
+    }
+    if (lane == 0) wtot[wave] = wsum;
+    __syncthreads();
+    uint32_t before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+        const uint32_t x = wtot[w];
+        before += (w < wave) ? x : 0;
+        total += x;
+    }
+    return before + mine;
+}
+
+// Count of candidates >= c1, c2, c3 among cand[i], i in [first, n) step
+// `step`, packed 21 bits each; wave-uniform.
+__device__ __forceinline__ uint64_t count3(const int32_t *cand, uint32_t first, uint32_t n, uint32_t step,
+                                           int32_t c1, int32_t c2, int32_t c3)
+{
+    uint32_t m1 = 0, m2 = 0, m3 = 0;
+    for (uint32_t b0 = 0; b0 < n; b0 += step) {
+        const uint32_t i = b0 + first;
+        const int32_t v = (i < n) ? cand[i] : -1;
+        m1 += __popcll(__ballot(v >= c1));
+        m2 += __popcll(__ballot(v >= c2));
+        m3 += __popcll(__ballot(v >= c3));
+    }
+    return (uint64_t)m1 | ((uint64_t)m2 << 21) | ((uint64_t)m3 << 42);
 }
 
 template <int KPT>
@@ -40,11 +98,15 @@ __global__ void __launch_bounds__(kSelectThreads)
 k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__ idx, int64_t ldidx,
          float *__restrict__ thresh, double *__restrict__ bound)
 {
-    constexpr int NW = kSelectThreads / 64;
-    __shared__ uint64_t red[2][NW];
-    __shared__ uint64_t wsum[NW];
-    __shared__ double fsum[NW];
-    __shared__ int32_t s_last;
+    __shared__ uint32_t hist[kBuckets];
+    __shared__ int32_t cand[KPT * kSelectThreads];
+    __shared__ uint64_t red[2][kNW];
+    __shared__ uint64_t wsum64[kNW];
+    __shared__ uint32_t wtot[2][kNW];
+    __shared__ float fmin[kNW], fmax[kNW];
+    __shared__ double fsum[kNW];
+    __shared__ int32_t s_last, s_bin, s_T;
+    __shared__ int64_t s_above;
 
     const int64_t grp = blockIdx.x;
     int64_t K, kk;
@@ -58,46 +120,142 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     }
     const float *s = scores + grp * sh.lds;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) s_last = 0;   // written again (by the kk-th keeper) after several barriers
     const int kpt = (int)((K + kSelectThreads - 1) / kSelectThreads);
     const int64_t base = (int64_t)tid * kpt;
 
-    int32_t key[KPT];  // -1 marks "no key here"; real keys are >= 0
+    for (int i = tid; i < kBuckets; i += kSelectThreads) hist[i] = 0;
+    if (tid == 0) s_last = 0;   // written again (by the kk-th keeper) after several barriers
+    int32_t key[KPT];           // -1 marks "no key here"; real keys are >= 0
+    float mn = __builtin_inff(), mx = 0.0f;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         const int64_t k = base + i;
         key[i] = (i < kpt && k < K) ? __float_as_int(s[k]) : -1;
-    }
-
-    // ---- 1. threshold search
-    int32_t T = 0;
-    int round = 0;
-    for (int sh2 = 29; sh2 >= 1; sh2 -= 2, ++round) {
-        const int32_t c1 = T | (1 << sh2), c2 = T | (2 << sh2), c3 = T | (3 << sh2);
-        uint32_t n1 = 0, n2 = 0, n3 = 0;   // wave-uniform counts
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            n1 += __popcll(__ballot(key[i] >= c1));
-            n2 += __popcll(__ballot(key[i] >= c2));
-            n3 += __popcll(__ballot(key[i] >= c3));
+        if (key[i] >= 0) {
+            mn = fminf(mn, __int_as_float(key[i]));
+            mx = fmaxf(mx, __int_as_float(key[i]));
         }
-        const uint64_t tot = block_sum_uniform((uint64_t)n1 | ((uint64_t)n2 << 21) | ((uint64_t)n3 << 42),
-                                               red[round & 1]);
-        const int64_t t1 = tot & 0x1fffff, t2 = (tot >> 21) & 0x1fffff, t3 = tot >> 42;
-        const int v = (t3 >= kk) ? 3 : (t2 >= kk) ? 2 : (t1 >= kk) ? 1 : 0;
-        T |= v << sh2;
     }
-    {
-        const int32_t c1 = T | 1;
-        uint32_t n1 = 0;
+    // ---- group min / max
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) n1 += __popcll(__ballot(key[i] >= c1));
-        const uint64_t tot = block_sum_uniform(n1, red[round & 1]);
-        if ((int64_t)tot >= kk) T = c1;
+    for (int m = 32; m >= 1; m >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, m, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    }
+    if (lane == 0) {
+        fmin[wave] = mn;
+        fmax[wave] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+        mn = fminf(mn, fmin[w]);
+        mx = fmaxf(mx, fmax[w]);
+    }
+    const float scale = (mx > mn) ? (float)kBuckets / (mx - mn) : 0.0f;
+    auto bucket = [&](int32_t k) -> int {
+        const int b = (int)((__int_as_float(k) - mn) * scale);
+        return b < kBuckets - 1 ? b : kBuckets - 1;
+    };
+
+    // ---- 1. value-range histogram, then the bucket holding the kk-th key
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+        if (key[i] >= 0) atomicAdd(&hist[bucket(key[i])], 1u);
+    __syncthreads();
+    {
+        // thread t owns buckets 2t, 2t+1
+        const uint32_t hlo = hist[2 * tid], hhi = hist[2 * tid + 1];
+        uint32_t total;
+        const uint32_t incl = block_excl_scan(hlo + hhi, wtot[0], total) + hlo + hhi;
+        const int64_t above = (int64_t)total - incl;   // keys in buckets above 2t+1
+        if (above < kk && kk <= above + hhi) {
+            s_bin = 2 * tid + 1;
+            s_above = above;
+        } else if (above + hhi < kk && kk <= above + hhi + hlo) {
+            s_bin = 2 * tid;
+            s_above = above + hhi;
+        }
+    }
+    __syncthreads();
+    const int bin = s_bin;
+    const int64_t need = kk - s_above;   // how many of the bucket's keys are kept (>= 1)
+
+    // ---- 2. the bucket's keys to LDS, then T among them
+    uint32_t nc = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) nc += (key[i] >= 0 && bucket(key[i]) == bin);
+    uint32_t n1;
+    uint32_t pos_c = block_excl_scan(nc, wtot[1], n1);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+        if (key[i] >= 0 && bucket(key[i]) == bin) cand[pos_c++] = key[i];
+    __syncthreads();
+    int32_t T = 0;
+    if (n1 <= 1024) {
+        // one wave, candidates held in registers (16 slots of 64)
+        if (wave == 0) {
+            int32_t c[16];
+            int32_t lo = 0x7fffffff, hi = 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t i = j * 64 + lane;
+                c[j] = (i < n1) ? cand[i] : -1;
+                if (c[j] >= 0) {
+                    lo = min(lo, c[j]);
+                    hi = max(hi, c[j]);
+                }
+            }
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) {
+                lo = min(lo, __shfl_xor(lo, m, 64));
+                hi = max(hi, __shfl_xor(hi, m, 64));
+            }
+            // lo <= T <= hi, so T shares their common high bits; search the rest
+            const int hb = (lo == hi) ? -1 : 31 - __clz(lo ^ hi);
+            T = (hb < 0) ? lo : (lo & ~((int32_t)((2u << hb) - 1u)));
+            const int nslots = (int)((n1 + 63) / 64);
+            int b = hb;
+            for (; b >= 1; b -= 2) {
+                const int32_t c1 = T | (1 << (b - 1)), c2 = T | (2 << (b - 1)), c3 = T | (3 << (b - 1));
+                uint32_t m1 = 0, m2 = 0, m3 = 0;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    if (j < nslots) {
+                        m1 += __popcll(__ballot(c[j] >= c1));
+                        m2 += __popcll(__ballot(c[j] >= c2));
+                        m3 += __popcll(__ballot(c[j] >= c3));
+                    }
+                }
+                T |= ((m3 >= need) ? 3 : (m2 >= need) ? 2 : (m1 >= need) ? 1 : 0) << (b - 1);
+            }
+            if (b == 0) {
+                uint32_t m1 = 0;
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (j < nslots) m1 += __popcll(__ballot(c[j] >= (T | 1)));
+                if (m1 >= need) T |= 1;
+            }
+            if (lane == 0) s_T = T;
+        }
+        __syncthreads();
+        T = s_T;
+    } else {
+        int round = 0;
+        for (int sh2 = 29; sh2 >= 1; sh2 -= 2, ++round) {
+            const uint64_t c = block_sum_uniform(
+                count3(cand, tid, n1, kSelectThreads, T | (1 << sh2), T | (2 << sh2), T | (3 << sh2)),
+                red[round & 1]);
+            const int64_t t1 = c & 0x1fffff, t2 = (c >> 21) & 0x1fffff, t3 = c >> 42;
+            T |= ((t3 >= need) ? 3 : (t2 >= need) ? 2 : (t1 >= need) ? 1 : 0) << sh2;
+        }
+        const uint64_t c = block_sum_uniform(count3(cand, tid, n1, kSelectThreads, T | 1, T | 1, T | 1),
+                                             red[round & 1]);
+        if ((int64_t)(c & 0x1fffff) >= need) T |= 1;
     }
 
-    // ---- 2. ordered compaction
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes < this one
+    // ---- 3. ordered compaction
+    const uint64_t below = lanes_below(lane);
     uint32_t gt_w = 0, eq_w = 0, gt_tot_w = 0, eq_tot_w = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -107,12 +265,12 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         gt_tot_w += __popcll(bg);
         eq_tot_w += __popcll(be);
     }
-    if (lane == 0) wsum[wave] = ((uint64_t)gt_tot_w << 32) | eq_tot_w;
+    if (lane == 0) wsum64[wave] = ((uint64_t)gt_tot_w << 32) | eq_tot_w;
     __syncthreads();
     uint64_t before = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint64_t x = wsum[w];
+    for (int w = 0; w < kNW; ++w) {
+        const uint64_t x = wsum64[w];
         before += (w < wave) ? x : 0;
         total += x;
     }
@@ -151,7 +309,7 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     for (int64_t j = kk + tid; j < padded; j += kSelectThreads) out[j] = s_last;
     if (bound && tid == 0) {
         double b = 0.0;
-        for (int w = 0; w < NW; ++w) b += fsum[w];
+        for (int w = 0; w < kNW; ++w) b += fsum[w];
         bound[grp] = b;
     }
 }
@@ -160,12 +318,16 @@ hipError_t launch_select(const float *scores, const SelectShape &sh, int32_t *id
                          float *thresh, double *bound, hipStream_t s)
 {
     dim3 grid((unsigned)sh.groups), block(kSelectThreads);
-    if (sh.K <= 4 * kSelectThreads)
-        hipLaunchKernelGGL(k_select<4>, grid, block, 0, s, scores, sh, idx, ldidx, thresh, bound);
-    else if (sh.K <= 16 * kSelectThreads)
-        hipLaunchKernelGGL(k_select<16>, grid, block, 0, s, scores, sh, idx, ldidx, thresh, bound);
-    else
-        hipLaunchKernelGGL(k_select<32>, grid, block, 0, s, scores, sh, idx, ldidx, thresh, bound);
+    const int64_t kpt = (sh.K + kSelectThreads - 1) / kSelectThreads;
+#define RMM_SELECT_LAUNCH(N) \
+    hipLaunchKernelGGL(k_select<N>, grid, block, 0, s, scores, sh, idx, ldidx, thresh, bound)
+    if (kpt <= 1) RMM_SELECT_LAUNCH(1);
+    else if (kpt <= 2) RMM_SELECT_LAUNCH(2);
+    else if (kpt <= 4) RMM_SELECT_LAUNCH(4);
+    else if (kpt <= 8) RMM_SELECT_LAUNCH(8);
+    else if (kpt <= 16) RMM_SELECT_LAUNCH(16);
+    else RMM_SELECT_LAUNCH(32);
+#undef RMM_SELECT_LAUNCH
     return hipGetLastError();
 }
 
