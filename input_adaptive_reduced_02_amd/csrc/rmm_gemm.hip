@@ -27,6 +27,9 @@
 #ifndef RMM_DL_WAVES
 #define RMM_DL_WAVES 8
 #endif
+#ifndef RMM_DL_WM
+#define RMM_DL_WM 2
+#endif
 #include "rmm_tile.h"
 
 namespace rmm {
@@ -193,18 +196,18 @@ hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_
     const int64_t kslab = (kk + 63) / 64 * 64;
     // DMA pipeline: every A row and index row must be readable up to the slab end
     if (rows > 64 && lda >= kslab && (!idx || ldidx >= kslab)) {
-        constexpr int NW = RMM_DL_WAVES;
-        using S = DlShape<NW>;
+        constexpr int NW = RMM_DL_WAVES, WMS = RMM_DL_WM;
+        using S = DlShape<NW, WMS>;
         const int64_t G = (M + group_rows - 1) / group_rows;
         const int tpg = (int)((rows + S::TM - 1) / S::TM);
         const int m_tiles = (int)(G * tpg);
         const int n_tiles = (int)((N + S::TN - 1) / S::TN);
         const int per = (m_tiles * n_tiles + 7) / 8;
         if (idx)
-            hipLaunchKernelGGL((k_gemm_dl<NW, true>), dim3((unsigned)(8 * per)), dim3(64 * NW), 0, s, A, lda, B,
+            hipLaunchKernelGGL((k_gemm_dl<NW, WMS, true>), dim3((unsigned)(8 * per)), dim3(64 * NW), 0, s, A, lda, B,
                                ldb, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy, tpg, m_tiles, n_tiles);
         else
-            hipLaunchKernelGGL((k_gemm_dl<NW, false>), dim3((unsigned)(8 * per)), dim3(64 * NW), 0, s, A, lda, B,
+            hipLaunchKernelGGL((k_gemm_dl<NW, WMS, false>), dim3((unsigned)(8 * per)), dim3(64 * NW), 0, s, A, lda, B,
                                ldb, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy, tpg, m_tiles, n_tiles);
         return hipGetLastError();
     }

@@ -32,12 +32,13 @@ namespace rmm {
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-// NW = 4: waves 2 x 2 of 64 x 128;  NW = 8: waves 2 x 4 of 64 x 64 (two waves
-// per SIMD, so one can feed the matrix core while the other waits on LDS).
-template <int NW>
+// NW waves arranged WMS (along M) x NW/WMS (along N).  Every wave reads the A
+// rows and B columns of its own sub-tile from LDS, so WMS = 1 reads each B
+// element (the half-rate transposed reads) once per slab and A NW times.
+template <int NW, int WMS>
 struct DlShape {
     static constexpr int TM = 128, TN = 256, BK = 64;
-    static constexpr int WAVES_M = 2, WAVES_N = NW / 2;
+    static constexpr int WAVES_M = WMS, WAVES_N = NW / WMS;
     static constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N, FM = WM / 32, FN = WN / 32;
     static constexpr int NSTAGE = 3;
     static constexpr int A_ELEMS = TM * BK;          // 16 KiB
@@ -73,13 +74,13 @@ __device__ __forceinline__ void dma4(const void *g, uint32_t lds)
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
-template <int NW, bool IDX>
+template <int NW, int WMS, bool IDX>
 __global__ void __launch_bounds__(64 * NW)
 k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
           const int32_t *__restrict__ idx, int64_t ldidx, int64_t M, int64_t N, int64_t kk, int64_t gr,
           void *__restrict__ Y, int ydt, int64_t ldy, int tiles_per_group, int m_tiles, int n_tiles)
 {
-    using S = DlShape<NW>;
+    using S = DlShape<NW, WMS>;
     constexpr int TM = S::TM, TN = S::TN, BK = S::BK, WM = S::WM, WN = S::WN, FM = S::FM, FN = S::FN;
     constexpr int AB = S::A_LOADS + S::B_LOADS;   // DMA loads per wave per slab
     constexpr int NT = 64 * NW;
@@ -130,7 +131,26 @@ k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
             dma4(I + j, iring0 + (kt % S::IDX_RING) * BK * 4);
         }
     };
-    // the A and B tiles of slab kt into ring stage kt % 3
+    // global addresses of slab kt's B rows, read from the index ring into
+    // registers (all ring reads before any DMA, so they share one LDS wait)
+    const uint16_t *b_row[S::B_LOADS];
+    auto prep_b = [&](int kt) {
+        const int64_t kbase = (int64_t)kt * BK;
+        int32_t kr[S::B_LOADS];
+#pragma unroll
+        for (int i = 0; i < S::B_LOADS; ++i) {
+            const int jr = (wave * S::B_LOADS + i) * 2 + h;  // row of the slab
+            if constexpr (IDX) kr[i] = iring[wave][kt % S::IDX_RING][jr];
+            else kr[i] = (int32_t)(kbase + jr);
+        }
+#pragma unroll
+        for (int i = 0; i < S::B_LOADS; ++i) {
+            const int jr = (wave * S::B_LOADS + i) * 2 + h;
+            const int64_t krow = (kbase + jr < kk) ? kr[i] : 0;   // past kk: row 0 (A is zero there)
+            b_row[i] = b_src[i] + krow * ldb;
+        }
+    };
+    // the A and B tiles of slab kt into ring stage kt % 3 (B rows from prep_b(kt))
     auto issue_ab = [&](int kt) {
         const int64_t kbase = (int64_t)kt * BK;
         const uint32_t sa = smem0 + (kt % S::NSTAGE) * S::STAGE_ELEMS * 2;
@@ -138,14 +158,7 @@ k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
 #pragma unroll
         for (int i = 0; i < S::A_LOADS; ++i) dma16(a_src[i] + kbase, sa + (wave * S::A_LOADS + i) * 1024);
 #pragma unroll
-        for (int i = 0; i < S::B_LOADS; ++i) {
-            const int jr = (wave * S::B_LOADS + i) * 2 + h;  // row of the slab
-            int64_t krow;
-            if constexpr (IDX) krow = iring[wave][kt % S::IDX_RING][jr];
-            else krow = kbase + jr;
-            if (kbase + jr >= kk) krow = 0;                // past kk: row 0 (A is zero there)
-            dma16(b_src[i] + krow * ldb, sb + (wave * S::B_LOADS + i) * 1024);
-        }
+        for (int i = 0; i < S::B_LOADS; ++i) dma16(b_row[i], sb + (wave * S::B_LOADS + i) * 1024);
     };
 
     floatx16 acc[FM][FN];
@@ -175,9 +188,13 @@ k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
     issue_idx(1);
     vmwait<0>();
     issue_idx(2);
+    prep_b(0);
     issue_ab(0);
     issue_idx(3);
-    if (nkt > 1) issue_ab(1);
+    if (nkt > 1) {
+        prep_b(1);
+        issue_ab(1);
+    }
 
     for (int kt = 0; kt < nkt; ++kt) {
         // slab kt must be in LDS; IDX(kt+3) and AB(kt+1) may stay in flight
@@ -186,9 +203,11 @@ k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
         } else {
             if (kt + 1 < nkt) vmwait<AB>(); else vmwait<0>();
         }
+        // slab kt landed, so did the index slab kt+2 (issued before it)
+        if (kt + 2 < nkt) prep_b(kt + 2);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         // every wave's slab kt landed, and stage (kt+2)%3 (slab kt-1) is free;
-        // index slot (kt+4)%4 held slab kt's indices, used two iterations ago
+        // index slot (kt+4)%4 held slab kt's indices, read two iterations ago
         issue_idx(kt + 4);
         if (kt + 2 < nkt) issue_ab(kt + 2);
         uint16_t *sa = smem + (kt % S::NSTAGE) * S::STAGE_ELEMS;

@@ -80,95 +80,60 @@ hipError_t launch_rownorms(const void *B, int dt, int64_t K, int64_t N, int64_t 
 }
 
 // ------------------------------------------------------------------ column scores
-// Grid (ceil(K / 512), G); each lane owns two adjacent columns of one group
-// and walks the group's rows top to bottom, UNROLL rows of loads in flight.
-constexpr int kColUnroll = 32;
+// Grid (ceil(K / 128), G), 128 lanes per workgroup; each lane owns one column
+// of one group and walks the group's rows top to bottom, the loads of up to
+// kColUnroll rows in flight (consecutive lanes read consecutive columns, so
+// every row load of a wave is one coalesced 128- or 256-byte segment).
+constexpr int kColUnroll = 64;
+constexpr int kColThreads = 128;
 
 template <int DT>
-__global__ void __launch_bounds__(256)
+__device__ __forceinline__ double load_elem(const void *p, int64_t i)
+{
+    if (DT == 1) return (double)bf16_to_f32(((const uint16_t *)p)[i]);
+    return (double)((const float *)p)[i];
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kColThreads)
 k_colscore(const void *__restrict__ Av, int64_t M, int64_t K, int64_t lda,
            const double *__restrict__ bnorm, int64_t gr, float *__restrict__ scores)
 {
     const int64_t g = blockIdx.y;
-    const int64_t c0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2;
-    if (c0 >= K) return;
+    const int64_t c = (int64_t)blockIdx.x * kColThreads + threadIdx.x;
+    if (c >= K) return;
     const int64_t r0 = g * gr;
     const int64_t rows = (M - r0 < gr) ? (M - r0) : gr;
-    const bool pair = (c0 + 1 < K);
-    double a0 = 0.0, a1 = 0.0;
-    if (DT == 1) {
-        const uint16_t *p = (const uint16_t *)Av + r0 * lda + c0;
-        if (pair) {
-            int64_t m = 0;
-            for (; m + kColUnroll <= rows; m += kColUnroll) {
-                uint32_t w[kColUnroll];
+    const char *p = (const char *)Av + (r0 * lda + c) * (DT == 1 ? 2 : 4);
+    const int64_t ld = lda * (DT == 1 ? 2 : 4);   // row stride in bytes
+    double a = 0.0;
+    int64_t m = 0;
+    for (; m + kColUnroll <= rows; m += kColUnroll) {
+        double x[kColUnroll];
 #pragma unroll
-                for (int u = 0; u < kColUnroll; ++u) w[u] = *(const uint32_t *)(p + (m + u) * lda);
+        for (int u = 0; u < kColUnroll; ++u) x[u] = load_elem<DT>(p + (m + u) * ld, 0);
 #pragma unroll
-                for (int u = 0; u < kColUnroll; ++u) {
-                    double lo = bf16_lo(w[u]), hi = bf16_hi(w[u]);
-                    a0 = __builtin_fma(lo, lo, a0);
-                    a1 = __builtin_fma(hi, hi, a1);
-                }
-            }
-            for (; m < rows; ++m) {
-                uint32_t w = *(const uint32_t *)(p + m * lda);
-                double lo = bf16_lo(w), hi = bf16_hi(w);
-                a0 = __builtin_fma(lo, lo, a0);
-                a1 = __builtin_fma(hi, hi, a1);
-            }
-        } else {
-            for (int64_t m = 0; m < rows; ++m) {
-                double x = bf16_to_f32(p[m * lda]);
-                a0 = __builtin_fma(x, x, a0);
-            }
-        }
-    } else {
-        const float *p = (const float *)Av + r0 * lda + c0;
-        if (pair) {
-            int64_t m = 0;
-            for (; m + kColUnroll <= rows; m += kColUnroll) {
-                float2 w[kColUnroll];
-#pragma unroll
-                for (int u = 0; u < kColUnroll; ++u) w[u] = *(const float2 *)(p + (m + u) * lda);
-#pragma unroll
-                for (int u = 0; u < kColUnroll; ++u) {
-                    double x0 = w[u].x, x1 = w[u].y;
-                    a0 = __builtin_fma(x0, x0, a0);
-                    a1 = __builtin_fma(x1, x1, a1);
-                }
-            }
-            for (; m < rows; ++m) {
-                float2 w = *(const float2 *)(p + m * lda);
-                double x0 = w.x, x1 = w.y;
-                a0 = __builtin_fma(x0, x0, a0);
-                a1 = __builtin_fma(x1, x1, a1);
-            }
-        } else {
-            for (int64_t m = 0; m < rows; ++m) {
-                double x = p[m * lda];
-                a0 = __builtin_fma(x, x, a0);
-            }
-        }
+        for (int u = 0; u < kColUnroll; ++u) a = __builtin_fma(x[u], x[u], a);
     }
-    float *out = scores + g * K + c0;
-    const double b0 = bnorm ? bnorm[c0] : 1.0;
-    out[0] = (float)(__builtin_sqrt(a0) * b0);
-    if (pair) {
-        const double b1 = bnorm ? bnorm[c0 + 1] : 1.0;
-        out[1] = (float)(__builtin_sqrt(a1) * b1);
+    for (; m < rows; ++m) {
+        const double x = load_elem<DT>(p + m * ld, 0);
+        a = __builtin_fma(x, x, a);
     }
+    const double b = bnorm ? bnorm[c] : 1.0;
+    scores[g * K + c] = (float)(__builtin_sqrt(a) * b);
 }
 
 hipError_t launch_colscore(const void *A, int dt, int64_t M, int64_t K, int64_t lda,
                            const double *bnorm, int64_t group_rows, float *scores, hipStream_t s)
 {
     const int64_t G = (M + group_rows - 1) / group_rows;
-    dim3 grid((unsigned)((K + 511) / 512), (unsigned)G);
+    dim3 grid((unsigned)((K + kColThreads - 1) / kColThreads), (unsigned)G);
     if (dt == 1)
-        hipLaunchKernelGGL(k_colscore<1>, grid, dim3(256), 0, s, A, M, K, lda, bnorm, group_rows, scores);
+        hipLaunchKernelGGL(k_colscore<1>, grid, dim3(kColThreads), 0, s, A, M, K, lda, bnorm, group_rows,
+                           scores);
     else
-        hipLaunchKernelGGL(k_colscore<0>, grid, dim3(256), 0, s, A, M, K, lda, bnorm, group_rows, scores);
+        hipLaunchKernelGGL(k_colscore<0>, grid, dim3(kColThreads), 0, s, A, M, K, lda, bnorm, group_rows,
+                           scores);
     return hipGetLastError();
 }
 

@@ -9,14 +9,16 @@
 // contiguous index range [t*kpt, (t+1)*kpt) in registers.  Scores are
 // non-negative binary32, so their bit patterns, read as int32, order like the
 // values.  The threshold T (the kk-th largest key) is found in two steps:
-//   1. Value-range histogram: with mn, mx the group's smallest and largest
-//      score, key v goes to bucket floor((v - mn) * 2048 / (mx - mn)), clamped
-//      to 2047.  Subtraction, multiplication by a positive constant and
-//      truncation are monotone in IEEE arithmetic, so the bucket index never
-//      decreases as v grows and equal keys share a bucket: the kk-th largest
-//      key lies in the bucket where the count from the top reaches kk.  Scores
-//      of a smooth distribution spread over many buckets, so the LDS atomics
-//      rarely collide and that bucket holds few keys.
+//   1. Bit-pattern histogram: with lo, hi the group's smallest and largest
+//      key, key u goes to bucket floor((u - lo) * 2048 / (hi - lo)), clamped
+//      to 2047, computed in binary32.  Conversion, multiplication by a
+//      positive constant and truncation are monotone, so the bucket index
+//      never decreases as u grows and equal keys share a bucket: the kk-th
+//      largest key lies in the bucket where the count from the top reaches kk.
+//      Buckets even in the bit pattern are roughly even in log(score), so
+//      outlier channels do not crowd the bulk of the scores into a few
+//      buckets; the LDS atomics rarely collide and the threshold's bucket
+//      holds few keys.
 //   2. The bucket's keys are copied to LDS and T is found among them bit by
 //      bit, two bits per round (three candidate prefixes counted with
 //      wavefront ballots).  Up to 1024 candidates one wave does this alone,
@@ -103,7 +105,7 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     __shared__ uint64_t red[2][kNW];
     __shared__ uint64_t wsum64[kNW];
     __shared__ uint32_t wtot[2][kNW];
-    __shared__ float fmin[kNW], fmax[kNW];
+    __shared__ int32_t imin[kNW], imax[kNW];
     __shared__ double fsum[kNW];
     __shared__ int32_t s_last, s_bin, s_T;
     __shared__ int64_t s_above;
@@ -126,39 +128,39 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     for (int i = tid; i < kBuckets; i += kSelectThreads) hist[i] = 0;
     if (tid == 0) s_last = 0;   // written again (by the kk-th keeper) after several barriers
     int32_t key[KPT];           // -1 marks "no key here"; real keys are >= 0
-    float mn = __builtin_inff(), mx = 0.0f;
+    int32_t lo = 0x7fffffff, hi = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         const int64_t k = base + i;
         key[i] = (i < kpt && k < K) ? __float_as_int(s[k]) : -1;
         if (key[i] >= 0) {
-            mn = fminf(mn, __int_as_float(key[i]));
-            mx = fmaxf(mx, __int_as_float(key[i]));
+            lo = min(lo, key[i]);
+            hi = max(hi, key[i]);
         }
     }
-    // ---- group min / max
+    // ---- group min / max of the keys
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, m, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+        lo = min(lo, __shfl_xor(lo, m, 64));
+        hi = max(hi, __shfl_xor(hi, m, 64));
     }
     if (lane == 0) {
-        fmin[wave] = mn;
-        fmax[wave] = mx;
+        imin[wave] = lo;
+        imax[wave] = hi;
     }
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kNW; ++w) {
-        mn = fminf(mn, fmin[w]);
-        mx = fmaxf(mx, fmax[w]);
+        lo = min(lo, imin[w]);
+        hi = max(hi, imax[w]);
     }
-    const float scale = (mx > mn) ? (float)kBuckets / (mx - mn) : 0.0f;
+    const float scale = (hi > lo) ? (float)kBuckets / (float)(hi - lo) : 0.0f;
     auto bucket = [&](int32_t k) -> int {
-        const int b = (int)((__int_as_float(k) - mn) * scale);
+        const int b = (int)((float)(k - lo) * scale);
         return b < kBuckets - 1 ? b : kBuckets - 1;
     };
 
-    // ---- 1. value-range histogram, then the bucket holding the kk-th key
+    // ---- 1. bit-pattern histogram, then the bucket holding the kk-th key
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
         if (key[i] >= 0) atomicAdd(&hist[bucket(key[i])], 1u);
