@@ -75,6 +75,11 @@ class Linear:
             self.B = torch.from_numpy(d["B"]).to(dev)
         self.f32 = d["dtype"] == "f32"
         self.bnorm = rmm.rmm_rownorms(self.B)   # once per weight, outside the timed step
+        # The decode weight's kept rows (141-470 MB) are the size of the
+        # 256 MB last-level cache; steps rotate over 3 copies of the weight so
+        # that every step streams it from HBM, as a real decode step would.
+        self.Bs = [self.B] + [self.B.clone() for _ in range(2 if name == "decode" else 0)]
+        self._rot = 0
         torch.cuda.synchronize()
         log(f"[bench] {name}: inputs {self.M}x{self.K} @ {self.K}x{self.N} ready in {time.time() - t0:.1f}s")
         self.G = -(-self.M // self.gr)
@@ -85,6 +90,11 @@ class Linear:
         return (f"{self.name}: X {self.M}x{self.K} {dt} @ W {self.K}x{self.N} {dt}, "
                 f"{self.gr}-row selection groups, r={r}")
 
+    def next_B(self):
+        """The weight copy the next GEMM reads (rotates for decode)."""
+        self._rot = (self._rot + 1) % len(self.Bs)
+        return self.Bs[self._rot]
+
     def stages(self, r):
         """[(name, fn)] of one step at ratio r, buffers allocated once here."""
         rmm, torch = self.rmm, self.torch
@@ -92,7 +102,7 @@ class Linear:
         self.kk = kk
         Y = torch.empty((self.M, self.N), dtype=torch.float32 if self.f32 else torch.bfloat16, device=self.dev)
         if kk == self.K and not self.f32:
-            return [("gemm", lambda: rmm.rmm_gemm(self.A, self.B, None, kk, self.gr, Y=Y))], kk
+            return [("gemm", lambda: rmm.rmm_gemm(self.A, self.next_B(), None, kk, self.gr, Y=Y))], kk
         kpad = rmm.rmm_kk_pad(kk)
         idx = torch.empty((self.G, kpad), dtype=torch.int32, device=self.dev)
         Ap = torch.empty((self.M, kpad), dtype=torch.bfloat16, device=self.dev)
@@ -106,7 +116,7 @@ class Linear:
                     ("gemm", lambda: rmm.rmm_gemm(Ap, Bp, None, kk, self.gr, Y=Y))], kk
         return [sel,
                 ("gather", lambda: rmm.rmm_gather(self.A, idx, kk, self.gr, Apanel=Ap)),
-                ("gemm", lambda: rmm.rmm_gemm(Ap, self.B, idx, kk, self.gr, Y=Y))], kk
+                ("gemm", lambda: rmm.rmm_gemm(Ap, self.next_B(), idx, kk, self.gr, Y=Y))], kk
 
     def flops(self, r):
         return 2.0 * self.M * self.rmm.rmm_kk(r, self.K) * self.N

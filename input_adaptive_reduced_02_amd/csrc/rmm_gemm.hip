@@ -23,6 +23,7 @@
 //   narrow   TM=64  TN=64  BK=256 waves 2x2 of 32x32    (<= 64 rows per group,
 //            e.g. decode: many N tiles stream the kept rows of a wide weight)
 #include "rmm_gemm_dl.h"
+#include "rmm_gemm_sk.h"
 
 #ifndef RMM_DL_WAVES
 #define RMM_DL_WAVES 8
@@ -209,6 +210,20 @@ hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_
         else
             hipLaunchKernelGGL((k_gemm_dl<NW, WMS, false>), dim3((unsigned)(8 * per)), dim3(64 * NW), 0, s, A, lda, B,
                                ldb, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy, tpg, m_tiles, n_tiles);
+        return hipGetLastError();
+    }
+    if (rows <= 64 && lda >= kslab && (!idx || ldidx >= kslab)) {
+        using S = SkShape;
+        const int64_t G = (M + group_rows - 1) / group_rows;
+        const int m_tiles = (int)G;
+        const int n_tiles = (int)((N + S::TN - 1) / S::TN);
+        const int per = (m_tiles * n_tiles + 7) / 8;
+        if (idx)
+            hipLaunchKernelGGL((k_gemm_sk<true>), dim3((unsigned)(8 * per)), dim3(64 * S::NW), 0, s, A, lda, B, ldb,
+                               idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy, 1, m_tiles, n_tiles);
+        else
+            hipLaunchKernelGGL((k_gemm_sk<false>), dim3((unsigned)(8 * per)), dim3(64 * S::NW), 0, s, A, lda, B, ldb,
+                               idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy, 1, m_tiles, n_tiles);
         return hipGetLastError();
     }
     if (rows <= 64)
