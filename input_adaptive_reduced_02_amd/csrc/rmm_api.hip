@@ -131,7 +131,7 @@ int rmm_gather(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const i
         if (!ok_matrix(B, dt, N, ldb) || N % 8 != 0) return RMM_EINVAL;
         if (!ok_matrix(Bpanel, RMM_BF16, N, ldbp)) return RMM_EINVAL;
     }
-    return hip_status(launch_gather(A, dt, M, lda, idx, ldidx, kk, group_rows, Apanel, ldp, B, N, ldb,
+    return hip_status(launch_gather(A, dt, M, K, lda, idx, ldidx, kk, group_rows, Apanel, ldp, B, N, ldb,
                                     Bpanel, ldbp, as_stream(stream)));
 }
 

@@ -6,9 +6,12 @@
 // plain 16-byte loads.  Optionally packs the kept rows B[I, :] as well (single
 // group only; the GEMM otherwise reads kept B rows in place by index).
 //
-// HBM-bound data movement.  Each thread produces 8 consecutive panel columns
-// of one row (one 16-byte store) from 8 ascending kept indices, so a wave's
-// loads of A fall within one row and its stores are fully coalesced.
+// HBM-bound data movement.  Picking 2-byte elements straight out of global
+// memory costs the load units a cache-line access per element, so whole rows
+// of A are first copied into LDS with coalesced 16-byte loads (a workgroup
+// holds up to 32 KiB of rows), then every thread picks 8 kept elements of a
+// row out of LDS by index and writes them as one 16-byte panel chunk.  The
+// global traffic is exactly one read of A and one write of the panel.
 #include "rmm_internal.h"
 
 namespace rmm {
@@ -56,6 +59,65 @@ k_gather_a(const void *__restrict__ Av, int64_t M, int64_t lda, const int32_t *_
     *(uint4 *)(Ap + m * ldp + j0) = o;
 }
 
+constexpr int kGatherLds = 32768;   // bytes of A rows staged per workgroup
+
+// One workgroup per `rpw` consecutive rows: the rows go to LDS (16-byte
+// chunks, the ragged end of a row element by element), then thread t writes
+// panel chunks t, t + 256, ... of every row.
+template <int DT>
+__global__ void __launch_bounds__(256)
+k_gather_rows(const void *__restrict__ Av, int64_t M, int64_t K, int64_t lda, const int32_t *__restrict__ idx,
+              int64_t ldidx, int64_t kk, int64_t gr, uint16_t *__restrict__ Ap, int64_t ldp, int rpw,
+              int row_bytes)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char stage[];
+    constexpr int ES = DT == 1 ? 2 : 4;
+    const int64_t m0 = (int64_t)blockIdx.x * rpw;
+    const int nrow = (int)((M - m0 < rpw) ? (M - m0) : rpw);
+    const int full = (int)(K * ES / 16);          // whole 16-byte chunks in a row
+    const int tid = threadIdx.x;
+    for (int r = 0; r < nrow; ++r) {
+        const unsigned char *src = (const unsigned char *)Av + (m0 + r) * lda * ES;
+        unsigned char *dst = stage + r * row_bytes;
+        for (int c = tid; c < full; c += 256) *(uint4 *)(dst + 16 * c) = *(const uint4 *)(src + 16 * c);
+        for (int64_t e = (int64_t)full * 16 / ES + tid; e < K; e += 256) {
+            if (DT == 1) ((uint16_t *)dst)[e] = ((const uint16_t *)src)[e];
+            else ((float *)dst)[e] = ((const float *)src)[e];
+        }
+    }
+    __syncthreads();
+    const int64_t cpr = pad_up(kk) / 8;
+    for (int r = 0; r < nrow; ++r) {
+        const int64_t m = m0 + r;
+        const int32_t *I = idx + (m / gr) * ldidx;
+        const unsigned char *row = stage + r * row_bytes;
+        uint16_t *out = Ap + m * ldp;
+        for (int64_t c = tid; c < cpr; c += 256) {
+            const int64_t j0 = c * 8;
+            uint32_t h[8];
+            if (j0 + 8 <= kk) {
+                const int4 i0 = *(const int4 *)(I + j0);
+                const int4 i1 = *(const int4 *)(I + j0 + 4);
+                const int32_t ks[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    h[e] = DT == 1 ? ((const uint16_t *)row)[ks[e]] : f32_to_bf16(((const float *)row)[ks[e]]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    h[e] = 0;
+                    if (j0 + e < kk) {
+                        const int32_t k = I[j0 + e];
+                        h[e] = DT == 1 ? ((const uint16_t *)row)[k] : f32_to_bf16(((const float *)row)[k]);
+                    }
+                }
+            }
+            *(uint4 *)(out + j0) =
+                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        }
+    }
+}
+
 // Bp[j][:] = bf16(B[idx[j]][:]) for j < kk, zero for kk <= j < kpad.
 template <int DT>
 __global__ void __launch_bounds__(256)
@@ -81,19 +143,35 @@ k_gather_b(const void *__restrict__ Bv, int64_t N, int64_t ldb, const int32_t *_
     *(uint4 *)(Bp + j * ldbp + n0) = o;
 }
 
-hipError_t launch_gather(const void *A, int dt, int64_t M, int64_t lda, const int32_t *idx,
+hipError_t launch_gather(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const int32_t *idx,
                          int64_t ldidx, int64_t kk, int64_t group_rows, uint16_t *Ap, int64_t ldp,
                          const void *B, int64_t N, int64_t ldb, uint16_t *Bp, int64_t ldbp,
                          hipStream_t s)
 {
     const int64_t kpad = pad_up(kk);
     const int64_t cpr = kpad / 8;
-    const int64_t threads = M * cpr;
-    dim3 grid((unsigned)((threads + 255) / 256));
-    if (dt == 1)
-        hipLaunchKernelGGL(k_gather_a<1>, grid, dim3(256), 0, s, A, M, lda, idx, ldidx, kk, group_rows, Ap, ldp, cpr);
-    else
-        hipLaunchKernelGGL(k_gather_a<0>, grid, dim3(256), 0, s, A, M, lda, idx, ldidx, kk, group_rows, Ap, ldp, cpr);
+    const int64_t row_bytes = (K * (dt == 1 ? 2 : 4) + 15) / 16 * 16;
+    if (row_bytes <= kGatherLds) {
+        int rpw = (int)(kGatherLds / row_bytes);
+        if (rpw > 8) rpw = 8;
+        const unsigned blocks = (unsigned)((M + rpw - 1) / rpw);
+        const size_t lds = (size_t)rpw * row_bytes;
+        if (dt == 1)
+            hipLaunchKernelGGL(k_gather_rows<1>, dim3(blocks), dim3(256), lds, s, A, M, K, lda, idx, ldidx, kk,
+                               group_rows, Ap, ldp, rpw, (int)row_bytes);
+        else
+            hipLaunchKernelGGL(k_gather_rows<0>, dim3(blocks), dim3(256), lds, s, A, M, K, lda, idx, ldidx, kk,
+                               group_rows, Ap, ldp, rpw, (int)row_bytes);
+    } else {
+        const int64_t threads = M * cpr;
+        dim3 grid((unsigned)((threads + 255) / 256));
+        if (dt == 1)
+            hipLaunchKernelGGL(k_gather_a<1>, grid, dim3(256), 0, s, A, M, lda, idx, ldidx, kk, group_rows, Ap, ldp,
+                               cpr);
+        else
+            hipLaunchKernelGGL(k_gather_a<0>, grid, dim3(256), 0, s, A, M, lda, idx, ldidx, kk, group_rows, Ap, ldp,
+                               cpr);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !Bp) return e;
     const int64_t cb = N / 8;

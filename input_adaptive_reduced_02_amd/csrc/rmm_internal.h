@@ -8,6 +8,8 @@
 
 namespace rmm {
 
+// native vector (not HIP's struct uint4): arrays of it stay in registers
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
@@ -88,7 +90,7 @@ struct SelectShape {
 };
 hipError_t launch_select(const float *scores, const SelectShape &sh, int32_t *idx, int64_t ldidx,
                          float *thresh, double *bound, hipStream_t s);
-hipError_t launch_gather(const void *A, int dt, int64_t M, int64_t lda, const int32_t *idx,
+hipError_t launch_gather(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const int32_t *idx,
                          int64_t ldidx, int64_t kk, int64_t group_rows, uint16_t *Ap, int64_t ldp,
                          const void *B, int64_t N, int64_t ldb, uint16_t *Bp, int64_t ldbp,
                          hipStream_t s);

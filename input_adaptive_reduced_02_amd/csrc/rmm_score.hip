@@ -138,64 +138,190 @@ hipError_t launch_colscore(const void *A, int dt, int64_t M, int64_t K, int64_t 
 }
 
 // ------------------------------------------------------------------ P.V scores
-// Grid (ceil(L / 256), H).  Lane = key k of head h.  First ||V[h][k][:]||_2
-// (ascending d), then for every query block g whose causal prefix contains k
-// the mass of P over the block's queries (ascending q), read from the
-// contiguous key-major row Pt[h][k][q0 .. q0+nq), 64 values in flight.
+// ||V[h][k][:]||_2 for every key: lane per key, ascending d, exact squares.
 __global__ void __launch_bounds__(256)
-k_pv_score(const uint16_t *__restrict__ Pt, const uint16_t *__restrict__ V, int64_t L, int64_t D,
-           int64_t qblock, int causal, double *__restrict__ vnorm, float *__restrict__ scores)
+k_pv_vnorm(const uint16_t *__restrict__ V, int64_t HL, int64_t D, double *__restrict__ vnorm)
 {
-    const int64_t h = blockIdx.y;
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= L) return;
-    const int64_t G = (L + qblock - 1) / qblock;
-    const uint16_t *vrow = V + (h * L + k) * D;
+    const int64_t hk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (hk >= HL) return;
+    const uint16_t *vrow = V + hk * D;
     double vv = 0.0;
     for (int64_t d = 0; d < D; d += 8) {
-        uint4 v = *(const uint4 *)(vrow + d);
+        const uint4 v = *(const uint4 *)(vrow + d);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            double lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
+            const double lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
             vv = __builtin_fma(lo, lo, vv);
             vv = __builtin_fma(hi, hi, vv);
         }
     }
-    const double vn = __builtin_sqrt(vv);
-    vnorm[h * L + k] = vn;
-    const uint16_t *prow = Pt + (h * L + k) * L;
-    float *srow = scores + (h * G) * L + k;
-    const int64_t g0 = causal ? k / qblock : 0;
-    for (int64_t g = g0; g < G; ++g) {
-        const int64_t q0 = g * qblock;
-        const int64_t nq = (L - q0 < qblock) ? (L - q0) : qblock;
+    vnorm[hk] = __builtin_sqrt(vv);
+}
+
+// Block masses times V norms.  Work item = (head h, query block g, 64 keys
+// k0 .. k0+63 of the block's candidate keys): uniform in size whatever the
+// causal prefix length.  Items of a head are numbered block by block; with a
+// causal mask block g holds ceil(K_g / 64) = 2(g+1) items (all blocks but the
+// last full when L is a multiple of 128), so item i of a head lies in the
+// block g with g(g+1) <= i < (g+1)(g+2).
+//
+// Persistent waves walk the items with a grid stride, visiting them in the
+// scattered order (i * perm) mod total (perm coprime to total) so that the
+// items in flight at one time belong to many blocks and heads.  For an item
+// the wave reads the 64 key-major segments Pt[h][k][q0 .. q0+128) (256 B
+// each) with 16-byte loads that cover four whole segments per instruction;
+// the segments then pass through a small LDS slice half by half (queries
+// 0..63, then 64..127) so that lane l can sum segment l in ascending q in
+// binary64 -- the order a sequential sum takes -- and write
+// (float)(mass * ||V_k||).  The loads of the next item are issued before the
+// current item is summed.  Items that are not full (a short last query block
+// or a prefix ending inside the 64 keys) take a plain per-lane path.
+constexpr int kPvPitch = 144;   // bytes per staged half segment: 128 + 16 (rows on distinct banks)
+
+struct PvItem {
+    int64_t h, g, k0, q0, nq, Kg;
+    bool full;
+};
+
+__device__ __forceinline__ PvItem pv_item(int64_t it, int64_t L, int64_t qb, int causal, int64_t G,
+                                          int64_t per_head)
+{
+    PvItem r;
+    r.h = it / per_head;
+    const int64_t rem = it - r.h * per_head;
+    const int64_t cpb = (L + 63) / 64;
+    if (causal) {
+        int64_t g = (int64_t)((__builtin_sqrtf(4.0f * (float)rem + 1.0f) - 1.0f) * 0.5f);
+        while (g > 0 && g * (g + 1) > rem) --g;
+        while ((g + 1) * (g + 2) <= rem) ++g;
+        if (g > G - 1) g = G - 1;
+        r.g = g;
+        r.k0 = (rem - g * (g + 1)) * 64;
+    } else {
+        r.g = rem / cpb;
+        r.k0 = (rem - r.g * cpb) * 64;
+    }
+    r.q0 = r.g * qb;
+    r.nq = (L - r.q0 < qb) ? (L - r.q0) : qb;
+    r.Kg = causal ? ((r.q0 + qb < L) ? r.q0 + qb : L) : L;
+    r.full = r.nq == 128 && r.k0 + 64 <= r.Kg;
+    return r;
+}
+
+__global__ void __launch_bounds__(256)
+k_pv_mass(const uint16_t *__restrict__ Pt, int64_t H, int64_t L, int64_t qblock, int causal,
+          const double *__restrict__ vnorm, float *__restrict__ scores, int64_t per_head, int64_t perm)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char seg[4][64 * kPvPitch + 64 * 16];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t G = (L + qblock - 1) / qblock;
+    const int64_t total = H * per_head;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    unsigned char *sw = seg[w];
+    const int c = lane & 15;
+    // staging destinations: lanes holding chunks 0..7 write them in the first
+    // half, the others in the second; the lanes not writing a half store to
+    // a private dummy slot (never read), so every store is wave-wide
+    unsigned char *real = sw + (lane >> 4) * kPvPitch + 16 * (c & 7);
+    unsigned char *dummy = sw + 64 * kPvPitch + 16 * lane;
+    const int step0 = (c < 8) ? 4 * kPvPitch : 0, step1 = (c < 8) ? 0 : 4 * kPvPitch;
+    unsigned char *d0 = (c < 8) ? real : dummy, *d1 = (c < 8) ? dummy : real;
+    auto wave_sync = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    int64_t it = (int64_t)blockIdx.x * 4 + w;
+    u32x4 v[16];
+    PvItem cur{};
+    if (it < total) {
+        cur = pv_item(it * perm % total, L, qblock, causal, G, per_head);
+        if (cur.full) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] = *(const u32x4 *)(Pt + (cur.h * L + cur.k0 + 4 * i + (lane >> 4)) * L + cur.q0 + 8 * c);
+        }
+    }
+    while (it < total) {
+        const int64_t nx = it + stride;
+        PvItem nxt{};
+        if (nx < total) nxt = pv_item(nx * perm % total, L, qblock, causal, G, per_head);
+        const int64_t k = cur.k0 + lane;
         double mass = 0.0;
-        int64_t i = 0;
-        for (; i + 64 <= nq; i += 64) {
-            uint4 v[8];
+        if (cur.full) {
+            u32x4 hi[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = *(const uint4 *)(prow + q0 + i + 8 * u);
+            for (int i = 0; i < 16; ++i) {
+                *(u32x4 *)(d0 + i * step0) = v[i];
+                hi[i] = v[i];
+            }
+            // the registers are free: start the next item's loads now
+            if (nx < total && nxt.full) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                for (int i = 0; i < 16; ++i)
+                    v[i] = *(const u32x4 *)(Pt + (nxt.h * L + nxt.k0 + 4 * i + (lane >> 4)) * L + nxt.q0 + 8 * c);
+            }
+            const unsigned char *row = sw + lane * kPvPitch;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    mass += (double)bf16_lo(w[j]);
-                    mass += (double)bf16_hi(w[j]);
+            for (int half = 0; half < 2; ++half) {
+                if (half == 1) {
+                    wave_sync();   // every lane has read the first half
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) *(u32x4 *)(d1 + i * step1) = hi[i];
+                }
+                wave_sync();       // the slice was written by other lanes of this wave
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const u32x4 x = *(const u32x4 *)(row + 16 * j);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        mass += (double)bf16_lo(x[e]);
+                        mass += (double)bf16_hi(x[e]);
+                    }
                 }
             }
+            wave_sync();           // every lane has read the slice before the next item
+        } else {
+            if (k < cur.Kg) {
+                const uint16_t *src = Pt + (cur.h * L + k) * L + cur.q0;
+                for (int64_t i = 0; i < cur.nq; ++i) mass += (double)bf16_to_f32(src[i]);
+            }
+            if (nx < total && nxt.full) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    v[i] = *(const u32x4 *)(Pt + (nxt.h * L + nxt.k0 + 4 * i + (lane >> 4)) * L + nxt.q0 + 8 * c);
+            }
         }
-        for (; i < nq; ++i) mass += (double)bf16_to_f32(prow[q0 + i]);
-        srow[g * L] = (float)(mass * vn);
+        if (k < cur.Kg) scores[(cur.h * G + cur.g) * L + k] = (float)(mass * vnorm[cur.h * L + k]);
+        cur = nxt;
+        it = nx;
     }
 }
 
 hipError_t launch_pv_score(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D,
                            int64_t qblock, int causal, double *vnorm, float *scores, hipStream_t s)
 {
-    dim3 grid((unsigned)((L + 255) / 256), (unsigned)H);
-    hipLaunchKernelGGL(k_pv_score, grid, dim3(256), 0, s, Pt, V, L, D, qblock, causal, vnorm, scores);
+    const int64_t HL = H * L;
+    hipLaunchKernelGGL(k_pv_vnorm, dim3((unsigned)((HL + 255) / 256)), dim3(256), 0, s, V, HL, D, vnorm);
+    const int64_t G = (L + qblock - 1) / qblock;
+    const int64_t cpb = (L + 63) / 64;
+    // items per head: causal blocks hold 2(g+1) items, the last ceil(L/64) - 2(G-1)
+    const int64_t per_head = causal ? (G - 1) * G + cpb : G * cpb;
+    const int64_t total = H * per_head;
+    int64_t blocks = (total + 3) / 4;
+    if (blocks > 1024) blocks = 1024;   // four 4-wave workgroups per CU (41 KiB of LDS each), persistent
+    // a prime coprime to the item count (item indices times it stay below 2^63)
+    int64_t perm = 1;
+    for (int64_t p : {1000003LL, 999983LL, 999979LL, 999961LL})
+        if (total % p != 0) {
+            perm = p % total;
+            break;
+        }
+    if (perm == 0) perm = 1;
+    hipLaunchKernelGGL(k_pv_mass, dim3((unsigned)blocks), dim3(256), 0, s, Pt, H, L, qblock, causal, vnorm, scores,
+                       per_head, perm);
     return hipGetLastError();
 }
 
