@@ -316,10 +316,231 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     }
 }
 
+// ------------------------------------------------------------------ one wave per group
+// Used when there are many groups.  For K <= 64 * 128 one wave holds a whole
+// group: key i = 64 j + lane sits in
+// register j of lane `lane`, so loads coalesce and the kept indices, taken
+// in (j, lane) order, come out ascending.  Same steps as above without any
+// workgroup barrier: bit-pattern histogram in LDS, the bucket holding the
+// kk-th largest key by a wave prefix scan, T by exact rank among that
+// bucket's keys (at most 64 of them; otherwise a 2-bit search over all keys),
+// then the ordered compaction with ballots (keys == T kept in index order
+// until kk).
+__device__ __forceinline__ int wave_min(int v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, 64));
+    return v;
+}
+__device__ __forceinline__ int wave_max(int v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, 64));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int KPT>
+__global__ void __launch_bounds__(64)
+k_select_wave(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__ idx, int64_t ldidx,
+              float *__restrict__ thresh, double *__restrict__ bound)
+{
+    __shared__ uint32_t hist[kBuckets];
+    __shared__ int32_t cand[64];
+    const int64_t grp = blockIdx.x;
+    int64_t K, kk;
+    if (sh.pv) {
+        const int64_t g = grp % sh.Gq;
+        K = sh.causal ? ((sh.qblock * (g + 1) < sh.K) ? sh.qblock * (g + 1) : sh.K) : sh.K;
+        kk = kk_rule(sh.r, K);
+    } else {
+        K = sh.K;
+        kk = sh.kk;
+    }
+    const float *s = scores + grp * sh.lds;
+    const int lane = threadIdx.x;
+    const uint64_t below = lanes_below(lane);
+
+    int32_t key[KPT];   // -1: no key
+    int32_t lo = 0x7fffffff, hi = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int64_t i = (int64_t)j * 64 + lane;
+        key[j] = (i < K) ? __float_as_int(s[i]) : -1;
+        if (key[j] >= 0) {
+            lo = min(lo, key[j]);
+            hi = max(hi, key[j]);
+        }
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+
+    int32_t T;
+    if (lo == hi) {
+        T = lo;   // every key equal
+    } else {
+        // ---- 1. histogram, bucket of the kk-th largest key
+        for (int b = lane; b < kBuckets; b += 64) hist[b] = 0;
+        wave_lds_sync();
+        const float scale = (float)kBuckets / (float)(hi - lo);
+        auto bucket = [&](int32_t k) -> int {
+            const int b = (int)((float)(k - lo) * scale);
+            return b < kBuckets - 1 ? b : kBuckets - 1;
+        };
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if (key[j] >= 0) atomicAdd(&hist[bucket(key[j])], 1u);
+        wave_lds_sync();
+        // lane l owns buckets 32 l .. 32 l + 31
+        uint32_t hb[32], mine = 0;
+#pragma unroll
+        for (int b = 0; b < 32; ++b) {
+            hb[b] = hist[32 * lane + b];
+            mine += hb[b];
+        }
+        // keys in the buckets of higher lanes
+        uint32_t incl = mine;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t x = __shfl_down(incl, d, 64);
+            if (lane + d < 64) incl += x;
+        }
+        int64_t cum = (int64_t)(incl - mine);
+        int bin = -1;
+        int64_t need = 0;
+#pragma unroll
+        for (int b = 31; b >= 0; --b) {
+            if (bin < 0 && cum < kk && kk <= cum + (int64_t)hb[b]) {
+                bin = 32 * lane + b;
+                need = kk - cum;
+            }
+            cum += hb[b];
+        }
+        const uint64_t who = __ballot(bin >= 0);
+        const int src = __builtin_ctzll(who);
+        bin = __shfl(bin, src, 64);
+        need = __shfl(need, src, 64);
+
+        // ---- 2. T among the bucket's keys
+        uint32_t nc = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) nc += (key[j] >= 0 && bucket(key[j]) == bin);
+        const uint32_t n1 = wave_sum(nc);
+        if (n1 <= 64) {
+            // compact the candidates into cand[0 .. n1)
+            uint32_t pos = 0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const bool in = key[j] >= 0 && bucket(key[j]) == bin;
+                const uint64_t m = __ballot(in);
+                if (in) cand[pos + __popcll(m & below)] = key[j];
+                pos += __popcll(m);
+            }
+            wave_lds_sync();
+            const int32_t mineK = lane < (int)n1 ? cand[lane] : -1;
+            uint32_t gt = 0, ge = 0;
+            for (uint32_t i = 0; i < n1; ++i) {
+                const int32_t x = cand[i];
+                gt += x > mineK;
+                ge += x >= mineK;
+            }
+            const uint64_t hit = __ballot(lane < (int)n1 && gt < need && need <= ge);
+            T = __shfl(mineK, __builtin_ctzll(hit), 64);
+        } else {
+            // many keys in one bucket: 2-bit search over all keys, starting
+            // below the high bits lo and hi share
+            const int hb2 = 31 - __clz(lo ^ hi);
+            T = lo & ~((int32_t)((2u << hb2) - 1u));
+            int b = hb2;
+            for (; b >= 1; b -= 2) {
+                const int32_t c1 = T | (1 << (b - 1)), c2 = T | (2 << (b - 1)), c3 = T | (3 << (b - 1));
+                uint32_t m1 = 0, m2 = 0, m3 = 0;
+#pragma unroll
+                for (int j = 0; j < KPT; ++j) {
+                    m1 += key[j] >= c1;
+                    m2 += key[j] >= c2;
+                    m3 += key[j] >= c3;
+                }
+                m1 = wave_sum(m1);
+                m2 = wave_sum(m2);
+                m3 = wave_sum(m3);
+                T |= ((m3 >= kk) ? 3 : (m2 >= kk) ? 2 : (m1 >= kk) ? 1 : 0) << (b - 1);
+            }
+            if (b == 0) {
+                uint32_t m1 = 0;
+#pragma unroll
+                for (int j = 0; j < KPT; ++j) m1 += key[j] >= (T | 1);
+                if ((int64_t)wave_sum(m1) >= kk) T |= 1;
+            }
+        }
+    }
+
+    // ---- 3. ordered compaction
+    uint32_t ngt = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) ngt += key[j] > T;
+    const int64_t need_eq = kk - (int64_t)wave_sum(ngt);   // >= 1 by the choice of T
+    int32_t *out = idx + grp * ldidx;
+    int64_t pos = 0, eq_seen = 0;
+    int32_t last = 0;
+    double dropped = 0.0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const bool gtk = key[j] > T, eqk = key[j] == T;
+        const uint64_t me = __ballot(eqk);
+        const bool keep = gtk || (eqk && eq_seen + __popcll(me & below) < need_eq);
+        const uint64_t mk = __ballot(keep);
+        if (keep) {
+            const int64_t p = pos + __popcll(mk & below);
+            if (p < kk) out[p] = j * 64 + lane;
+        } else if (key[j] >= 0) {
+            dropped += (double)__int_as_float(key[j]);
+        }
+        if (mk) last = j * 64 + 63 - __clzll(mk);   // highest kept index so far
+        pos += __popcll(mk);
+        eq_seen += __popcll(me);
+    }
+    const int64_t padded = pad_up(kk);
+    for (int64_t j = kk + lane; j < padded; j += 64) out[j] = last;
+    if (thresh && lane == 0) thresh[grp] = __int_as_float(T);
+    if (bound) {
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) dropped += __shfl_xor(dropped, m, 64);
+        if (lane == 0) bound[grp] = dropped;
+    }
+}
+
 hipError_t launch_select(const float *scores, const SelectShape &sh, int32_t *idx, int64_t ldidx,
                          float *thresh, double *bound, hipStream_t s)
 {
     dim3 grid((unsigned)sh.groups), block(kSelectThreads);
+    // Many groups (the P.V blocks): one wave per group, many groups per CU at
+    // once -- throughput.  Few groups: one 1024-thread workgroup each, whose
+    // 16 waves finish a group sooner than a single wave does -- latency.
+    if (sh.groups >= 512 && sh.K <= 64 * 128) {
+        const int64_t kw = (sh.K + 63) / 64;
+#define RMM_SELECT_WAVE(N) \
+    hipLaunchKernelGGL(k_select_wave<N>, grid, dim3(64), 0, s, scores, sh, idx, ldidx, thresh, bound)
+        if (kw <= 4) RMM_SELECT_WAVE(4);
+        else if (kw <= 8) RMM_SELECT_WAVE(8);
+        else if (kw <= 16) RMM_SELECT_WAVE(16);
+        else if (kw <= 32) RMM_SELECT_WAVE(32);
+        else if (kw <= 64) RMM_SELECT_WAVE(64);
+        else RMM_SELECT_WAVE(128);
+#undef RMM_SELECT_WAVE
+        return hipGetLastError();
+    }
     const int64_t kpt = (sh.K + kSelectThreads - 1) / kSelectThreads;
 #define RMM_SELECT_LAUNCH(N) \
     hipLaunchKernelGGL(k_select<N>, grid, block, 0, s, scores, sh, idx, ldidx, thresh, bound)

@@ -236,3 +236,30 @@ def test_full_size(workload, r):
     Yref = np.stack([O.reduced(c["A64"], c["B64"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
     Sabs = np.stack([O.reduced(c["A64abs"], c["B64abs"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
     check_output(Yg[rows], Yref, Sabs, kk, tag + f" ({len(rows)} rows)")
+
+
+@pytest.mark.parametrize("case", [("attn_proj", 4096, 1000, 8, 8, 0.3), ("decode", 2048, 3000, 8, 4, 0.5),
+                                  ("mlp_down", 1024, 256, 8, 2, 0.7)],
+                         ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-g{c[4]}-r{c[5]}")
+def test_select_many_groups(case):
+    """512 or more groups take the one-wave-per-group select: scores, kept sets,
+    thresholds and bounds against the oracle, including groups of 2 rows whose
+    scores repeat and groups where every key is equal (rows of zeros)."""
+    workload, M, K, N, gr, r = case
+    tag = f"many groups {workload} {M}x{K} gr={gr} r={r}"
+    log(f"case {tag}")
+    c = make_case(workload, M, K, N, seed=5)
+    A = c["A"].clone()
+    A[: 3 * gr] = 0   # three all-zero groups: every score 0, ties broken by index
+    c = dict(c, A=A, A64=np.where(np.arange(M)[:, None] < 3 * gr, 0.0, c["A64"]))
+    assert -(-M // gr) >= 512
+    bnorm = rmm.rmm_rownorms(c["B"])
+    kk = rmm.rmm_kk(r, K)
+    G = -(-M // gr)
+    scores = torch.empty((G, K), dtype=torch.float32, device=DEV)
+    thresh = torch.empty(G, dtype=torch.float32, device=DEV)
+    bound = torch.empty(G, dtype=torch.float64, device=DEV)
+    idx = torch.zeros((G, rmm.rmm_kk_pad(kk)), dtype=torch.int32, device=DEV)
+    rmm.rmm_select(A, r, gr, bnorm=bnorm, idx=idx, scores=scores, thresh=thresh, bound=bound)
+    check_index_range(idx, K)
+    check_selection(c, r, gr, bnorm, idx, scores, thresh, bound, tag)
