@@ -129,6 +129,8 @@ class Linear:
         return 2.0 * kk * self.N + 2.0 * self.M * kk + yb * self.M * self.N
 
     bound = property(lambda self: "hbm" if self.name == "decode" else "mfma")
+    # the kernel the reduced GEMM runs on (groups of at most 64 rows: the decode kernel)
+    kernel = property(lambda self: "rmm::k_gemm_sk" if self.gr <= 64 else "rmm::k_gemm_dl")
 
     def cpu_baseline(self, r, groups):
         """The oracle (single-threaded fp64 C) on `groups` row groups at ratio r:
@@ -182,10 +184,14 @@ class PV:
     def stages(self, r):
         rmm, torch = self.rmm, self.torch
         O_ = torch.empty((self.H, self.L, self.D), dtype=torch.bfloat16, device=self.dev)
-        need = rmm.rmm_attn_pv_workspace_bytes(self.H, self.L, self.D, r)
-        ws = torch.empty(max(1, need), dtype=torch.uint8, device=self.dev)
         self.kk = max(self._kks(r))
-        return [("attn_pv", lambda: rmm.rmm_attn_pv(self.Pt, self.V, r, O=O_, ws=ws))], self.kk
+        if r >= 1.0:
+            return [("gemm", lambda: rmm.rmm_pv_gemm(self.Pt, self.V, 1.0, None, O=O_))], self.kk
+        idx = torch.empty((self.H * self.G, rmm.rmm_kk_pad(self.L)), dtype=torch.int32, device=self.dev)
+        need = rmm.rmm_attn_pv_workspace_bytes(self.H, self.L, self.D, r, have_idx_out=True)
+        ws = torch.empty(max(1, need), dtype=torch.uint8, device=self.dev)
+        return [("select", lambda: rmm.rmm_pv_select(self.Pt, self.V, r, idx_out=idx, ws=ws)),
+                ("gemm", lambda: rmm.rmm_pv_gemm(self.Pt, self.V, r, idx, O=O_))], self.kk
 
     def flops(self, r):
         return sum(2.0 * 128 * kk * self.D for kk in self._kks(r)) * self.H
@@ -195,6 +201,7 @@ class PV:
         return kept_p + 2.0 * 2 * self.H * self.L * self.D   # + V once, + O once
 
     bound = property(lambda self: "hbm")
+    kernel = "rmm::k_pv_gemm"
 
     def cpu_baseline(self, r, groups):
         import numpy as np
@@ -253,14 +260,18 @@ def time_stages(torch, stages, steps, warmup):
 
 
 # ------------------------------------------------------------------ HBM traffic
-GEMM_SOURCES = ["rmm_gemm.hip", "rmm_gemm_dl.h", "rmm_tile.h", "rmm_internal.h"]
+# sources of the kernel the roofline is taken on, per workload family
+GEMM_SOURCES = {
+    "linear": ["rmm_gemm.hip", "rmm_gemm_dl.h", "rmm_gemm_sk.h", "rmm_tile.h", "rmm_internal.h"],
+    "pv": ["rmm_pv.hip", "rmm_tile.h", "rmm_internal.h"],
+}
 
 
-def gemm_source_hash():
-    """sha256 over the reduced-GEMM kernel sources, in a fixed order."""
+def gemm_source_hash(family="linear"):
+    """sha256 over the GEMM kernel sources of a workload family, in a fixed order."""
     import hashlib
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in GEMM_SOURCES[family]:
         with open(os.path.join(ROOT, "input_adaptive_reduced_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -279,7 +290,8 @@ def measured_traffic(workload, r):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.strip()
-    if rec.get("source_sha256") != gemm_source_hash():
+    family = "pv" if workload.startswith("pv") else "linear"
+    if rec.get("source_sha256") != gemm_source_hash(family):
         return None
     try:
         return float(rec["traffic_bytes_per_launch"])
@@ -337,7 +349,7 @@ def main():
             + f", gemm {per_r[r]['gemm_tflops']:.1f} TFLOP/s {per_r[r]['gemm_gbs']:.0f} GB/s")
         del stages
     base = per_r[1.0]
-    gname = "gemm" if "gemm" in base["stage_ms"] else "attn_pv"
+    gname = "gemm"
     for r, v in per_r.items():
         v["speedup_step_vs_r1"] = base["ms_per_step"] / v["ms_per_step"]
         v["speedup_gemm_vs_r1"] = base["stage_ms"][gname] / v["stage_ms"][gname]
@@ -354,7 +366,7 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4),
                     traffic=measured_traffic(W.name, headline))
-    roof["kernel"] = gname
+    roof["kernel"] = W.kernel
     roof["kernel_ms"] = round(gemm_ms, 5)
 
     cpu = None

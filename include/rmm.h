@@ -181,6 +181,28 @@ int rmm_attn_pv(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int
                 int64_t qblock, int causal, void *O, int odt, int32_t *idx_out,
                 int64_t ldidx_out, float *scores_out, void *ws, size_t ws_bytes, void *stream);
 
+/* The two halves of rmm_attn_pv, for callers that score once and multiply
+ * later, or time the product alone.
+ *
+ * rmm_pv_select: the block scores and kept-key lists of rmm_attn_pv (same
+ * definitions, same layouts), without the product.  idx_out is required
+ * (ldidx_out % 4 == 0, >= rmm_kk_pad(L)); 0 < r < 1.  Workspace:
+ * rmm_attn_pv_workspace_bytes(H, L, D, r, qblock, causal, 1, scores_out != NULL)
+ * bytes.  Errors and supported shapes as rmm_attn_pv. */
+int rmm_pv_select(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D, double r,
+                  int64_t qblock, int causal, int32_t *idx_out, int64_t ldidx_out, float *scores_out,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* rmm_pv_gemm: O[h][q][:] = sum over the kept keys k of block g of
+ * P[h][q][k] * V[h][k][:], the kept keys of (h, g) being the first
+ * rmm_kk(r, K_g) entries of idx[h*G + g][:] (ascending, as rmm_pv_select
+ * writes them, ldidx % 4 == 0).  idx == NULL: every key of the causal prefix
+ * (the dense product; r is then ignored).  No workspace.  Errors and
+ * supported shapes as rmm_attn_pv. */
+int rmm_pv_gemm(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D, double r,
+                int64_t qblock, int causal, const int32_t *idx, int64_t ldidx, void *O, int odt,
+                void *stream);
+
 #ifdef __cplusplus
 }
 #endif

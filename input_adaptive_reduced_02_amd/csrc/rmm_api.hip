@@ -166,41 +166,33 @@ size_t rmm_attn_pv_workspace_bytes(int64_t H, int64_t L, int64_t D, double r, in
     return n;
 }
 
-int rmm_attn_pv(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D, double r,
-                int64_t qblock, int causal, void *O, int odt, int32_t *idx_out, int64_t ldidx_out,
-                float *scores_out, void *ws, size_t ws_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// argument checks shared by the P.V entry points; RMM_OK when all hold
+int pv_check(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D, int64_t qblock)
 {
     if (H < 1 || L < 1 || D < 1 || qblock < 1) return RMM_EINVAL;
     if (!Pt || !V || !aligned16(Pt) || !aligned16(V)) return RMM_EINVAL;
-    if (!(r > 0.0) || !(r <= 1.0)) return RMM_EINVAL;
-    if (!O || elem_size(odt) == 0 || !aligned16(O)) return RMM_EINVAL;
-    if (scores_out && !aligned4(scores_out)) return RMM_EINVAL;
-    const int64_t G = (L + qblock - 1) / qblock;
-    if (idx_out && (!aligned16(idx_out) || ldidx_out % 4 != 0 || ldidx_out < pad_up(L)))
-        return RMM_EINVAL;
-    if (D != 128 || qblock != 128 || L % 8 != 0 || L > kSelectMaxK) return RMM_EUNSUPPORTED;
-    const bool dense = r >= 1.0;
-    const size_t need = rmm_attn_pv_workspace_bytes(H, L, D, r, qblock, causal, idx_out != nullptr,
-                                                    scores_out != nullptr);
-    if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
+    return RMM_OK;
+}
 
-    hipStream_t s = as_stream(stream);
-    if (dense)
-        return hip_status(launch_pv_gemm(Pt, V, H, L, qblock, causal, 1.0, nullptr, 0, O, odt, s));
-    char *w = (char *)ws;
+int pv_shape_supported(int64_t L, int64_t D, int64_t qblock)
+{
+    return D == 128 && qblock == 128 && L % 8 == 0 && L <= kSelectMaxK;
+}
+
+// scores + kept-key lists into caller buffers (workspace carved as documented)
+int pv_select_impl(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D, double r,
+                   int64_t qblock, int causal, int32_t *ix, int64_t ldix, float *scores_out, char *w,
+                   hipStream_t s)
+{
+    const int64_t G = (L + qblock - 1) / qblock;
     double *vnorm = (double *)w;
     w += align_up((size_t)H * L * sizeof(double));
     float *sc = scores_out;
-    if (!sc) {
-        sc = (float *)w;
-        w += align_up((size_t)H * G * L * sizeof(float));
-    }
-    int32_t *ix = idx_out;
-    int64_t ldix = ldidx_out;
-    if (!ix) {
-        ix = (int32_t *)w;
-        ldix = pad_up(L);
-    }
+    if (!sc) sc = (float *)w;
     if (hipError_t e = launch_pv_score(Pt, V, H, L, D, qblock, causal, vnorm, sc, s)) return hip_status(e);
     SelectShape sh{};
     sh.groups = H * G;
@@ -211,8 +203,75 @@ int rmm_attn_pv(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int
     sh.qblock = qblock;
     sh.causal = causal;
     sh.r = r;
-    if (hipError_t e = launch_select(sc, sh, ix, ldix, nullptr, nullptr, s)) return hip_status(e);
+    return hip_status(launch_select(sc, sh, ix, ldix, nullptr, nullptr, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int rmm_attn_pv(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D, double r,
+                int64_t qblock, int causal, void *O, int odt, int32_t *idx_out, int64_t ldidx_out,
+                float *scores_out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (int e = pv_check(Pt, V, H, L, D, qblock)) return e;
+    if (!(r > 0.0) || !(r <= 1.0)) return RMM_EINVAL;
+    if (!O || elem_size(odt) == 0 || !aligned16(O)) return RMM_EINVAL;
+    if (scores_out && !aligned4(scores_out)) return RMM_EINVAL;
+    if (idx_out && (!aligned16(idx_out) || ldidx_out % 4 != 0 || ldidx_out < pad_up(L)))
+        return RMM_EINVAL;
+    if (!pv_shape_supported(L, D, qblock)) return RMM_EUNSUPPORTED;
+    const bool dense = r >= 1.0;
+    const size_t need = rmm_attn_pv_workspace_bytes(H, L, D, r, qblock, causal, idx_out != nullptr,
+                                                    scores_out != nullptr);
+    if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
+
+    hipStream_t s = as_stream(stream);
+    if (dense)
+        return hip_status(launch_pv_gemm(Pt, V, H, L, qblock, causal, 1.0, nullptr, 0, O, odt, s));
+    const int64_t G = (L + qblock - 1) / qblock;
+    char *w = (char *)ws;
+    // workspace: V norms, then scores (unless given), then kept keys (unless given)
+    char *after = w + align_up((size_t)H * L * sizeof(double));
+    if (!scores_out) after += align_up((size_t)H * G * L * sizeof(float));
+    int32_t *ix = idx_out;
+    int64_t ldix = ldidx_out;
+    if (!ix) {
+        ix = (int32_t *)after;
+        ldix = pad_up(L);
+    }
+    if (int e = pv_select_impl(Pt, V, H, L, D, r, qblock, causal, ix, ldix, scores_out, w, s)) return e;
     return hip_status(launch_pv_gemm(Pt, V, H, L, qblock, causal, r, ix, ldix, O, odt, s));
+}
+
+int rmm_pv_select(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D, double r,
+                  int64_t qblock, int causal, int32_t *idx_out, int64_t ldidx_out, float *scores_out,
+                  void *ws, size_t ws_bytes, void *stream)
+{
+    if (int e = pv_check(Pt, V, H, L, D, qblock)) return e;
+    if (!(r > 0.0) || !(r < 1.0)) return RMM_EINVAL;
+    if (!idx_out || !aligned16(idx_out) || ldidx_out % 4 != 0 || ldidx_out < pad_up(L)) return RMM_EINVAL;
+    if (scores_out && !aligned4(scores_out)) return RMM_EINVAL;
+    if (!pv_shape_supported(L, D, qblock)) return RMM_EUNSUPPORTED;
+    const size_t need = rmm_attn_pv_workspace_bytes(H, L, D, r, qblock, causal, 1, scores_out != nullptr);
+    if (need > ws_bytes || !ws || !aligned16(ws)) return RMM_EINVAL;
+    return pv_select_impl(Pt, V, H, L, D, r, qblock, causal, idx_out, ldidx_out, scores_out, (char *)ws,
+                          as_stream(stream));
+}
+
+int rmm_pv_gemm(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D, double r,
+                int64_t qblock, int causal, const int32_t *idx, int64_t ldidx, void *O, int odt,
+                void *stream)
+{
+    if (int e = pv_check(Pt, V, H, L, D, qblock)) return e;
+    if (!O || elem_size(odt) == 0 || !aligned16(O)) return RMM_EINVAL;
+    if (idx) {
+        if (!(r > 0.0) || !(r <= 1.0)) return RMM_EINVAL;
+        if (!aligned16(idx) || ldidx % 4 != 0 || ldidx < pad_up(L)) return RMM_EINVAL;
+    }
+    if (!pv_shape_supported(L, D, qblock)) return RMM_EUNSUPPORTED;
+    return hip_status(launch_pv_gemm(Pt, V, H, L, qblock, causal, idx ? r : 1.0, idx, idx ? ldidx : 0, O, odt,
+                                     as_stream(stream)));
 }
 
 }  // extern "C"

@@ -70,6 +70,10 @@ def _declare(L):
     L.rmm_attn_pv_workspace_bytes.argtypes = [_L, _L, _L, _Dbl, _L, _I, _I, _I]
     L.rmm_attn_pv.restype = _I
     L.rmm_attn_pv.argtypes = [_P, _P, _L, _L, _L, _Dbl, _L, _I, _P, _I, _P, _L, _P, _P, _S, _P]
+    L.rmm_pv_select.restype = _I
+    L.rmm_pv_select.argtypes = [_P, _P, _L, _L, _L, _Dbl, _L, _I, _P, _L, _P, _P, _S, _P]
+    L.rmm_pv_gemm.restype = _I
+    L.rmm_pv_gemm.argtypes = [_P, _P, _L, _L, _L, _Dbl, _L, _I, _P, _L, _P, _I, _P]
     return L
 
 
@@ -211,6 +215,34 @@ def rmm_attn_pv(Pt, V, r, qblock=128, causal=True, O=None, odt=torch.bfloat16, i
     _check("rmm_attn_pv", lib().rmm_attn_pv(
         _ptr(Pt), _ptr(V), H, L, D, float(r), qblock, int(bool(causal)), _ptr(O), _dt(O), _ptr(idx_out),
         ldix, _ptr(scores_out), _ptr(w), need, _stream(V)))
+    return O
+
+
+def rmm_pv_select(Pt, V, r, qblock=128, causal=True, idx_out=None, scores_out=None, ws=None):
+    """Kept-key lists [H*G, pad(L)] int32 of P.V (the scoring and selection of
+    rmm_attn_pv without the product)."""
+    H, L, D = V.shape
+    G = -(-L // qblock)
+    if idx_out is None:
+        idx_out = torch.empty((H * G, rmm_kk_pad(L)), dtype=torch.int32, device=V.device)
+    need = rmm_attn_pv_workspace_bytes(H, L, D, r, qblock, causal, True, scores_out is not None)
+    w = _ws(need, V.device, ws)
+    _check("rmm_pv_select", lib().rmm_pv_select(
+        _ptr(Pt), _ptr(V), H, L, D, float(r), qblock, int(bool(causal)), _ptr(idx_out), idx_out.stride(0),
+        _ptr(scores_out), _ptr(w), need, _stream(V)))
+    return idx_out
+
+
+def rmm_pv_gemm(Pt, V, r, idx=None, qblock=128, causal=True, O=None, odt=torch.bfloat16):
+    """O [H, L, D] = P.V over the kept keys idx (rmm_pv_select's lists); idx
+    None: the dense causal product."""
+    H, L, D = V.shape
+    if O is None:
+        O = torch.empty((H, L, D), dtype=odt, device=V.device)
+    ldix = idx.stride(0) if idx is not None else 0
+    _check("rmm_pv_gemm", lib().rmm_pv_gemm(
+        _ptr(Pt), _ptr(V), H, L, D, float(r), qblock, int(bool(causal)), _ptr(idx), ldix, _ptr(O), _dt(O),
+        _stream(V)))
     return O
 
 

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -155,3 +155,12 @@ def test_validation_rejects_bad_arguments():
     assert L.rmm_attn_pv(P, P2, 1, 256, 128, 1.0, 64, 1, P3, BF, None, 0, None, None, 0, None) == EUNSUP   # qblock
     assert L.rmm_attn_pv(P, P2, 1, 100, 128, 1.0, 128, 1, P3, BF, None, 0, None, None, 0, None) == EUNSUP  # L % 8
     assert L.rmm_attn_pv(P, P2, 1, 256, 128, 0.5, 128, 1, P3, BF, P, 100, None, P3, 1 << 30, None) == EINVAL  # ldix
+    # pv_select(Pt, V, H, L, D, r, qb, causal, idx_out, ldix, scores_out, ws, wsb, stream)
+    assert L.rmm_pv_select(P, P2, 1, 256, 128, 0.5, 128, 1, None, 256, None, P3, 1 << 30, None) == EINVAL  # no idx
+    assert L.rmm_pv_select(P, P2, 1, 256, 128, 1.0, 128, 1, P, 256, None, P3, 1 << 30, None) == EINVAL  # r == 1
+    assert L.rmm_pv_select(P, P2, 1, 256, 128, 0.5, 128, 1, P, 256, None, P3, 16, None) == EINVAL  # short ws
+    assert L.rmm_pv_select(P, P2, 1, 256, 64, 0.5, 128, 1, P, 256, None, P3, 1 << 30, None) == EUNSUP  # D
+    # pv_gemm(Pt, V, H, L, D, r, qb, causal, idx, ldidx, O, odt, stream)
+    assert L.rmm_pv_gemm(P, P2, 1, 256, 128, 0.5, 128, 1, P, 100, P3, BF, None) == EINVAL  # ldidx
+    assert L.rmm_pv_gemm(P, P2, 1, 256, 128, 0.5, 128, 1, None, 0, None, BF, None) == EINVAL  # no O
+    assert L.rmm_pv_gemm(P, P2, 1, 100, 128, 1.0, 128, 1, None, 0, P3, BF, None) == EUNSUP  # L % 8

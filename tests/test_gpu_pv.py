@@ -121,3 +121,25 @@ def test_pv_full(L, r):
         check_output(np.concatenate([o[0] for o in outs]), np.concatenate([o[1] for o in outs]),
                      np.concatenate([o[2] for o in outs]), max(o[3] for o in outs), f"{tag} h={h}")
     del O_, idx, scores
+
+
+@pytest.mark.parametrize("L,r", [(520, 0.3), (1024, 0.5)])
+def test_split_entry_points_match(L, r):
+    """rmm_pv_select then rmm_pv_gemm give the kept lists, scores and output of
+    rmm_attn_pv bit for bit (the same kernels), and rmm_pv_gemm without a list
+    equals the r = 1 product."""
+    H = 3
+    Pt, V = make_pv(H, L, seed=11)
+    O1, idx1, sc1 = run_pv(Pt, V, r)
+    G = -(-L // QB)
+    idx2 = torch.zeros_like(idx1)
+    sc2 = torch.zeros_like(sc1)
+    rmm.rmm_pv_select(Pt, V, r, QB, True, idx_out=idx2, scores_out=sc2)
+    O2 = rmm.rmm_pv_gemm(Pt, V, r, idx2, QB, True)
+    Od = rmm.rmm_pv_gemm(Pt, V, 1.0, None, QB, True)
+    Od_ref = rmm.rmm_attn_pv(Pt, V, 1.0, QB, True)
+    torch.cuda.synchronize()
+    assert torch.equal(sc1, sc2) and torch.equal(idx1, idx2)
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))
+    assert torch.equal(Od.view(torch.int16), Od_ref.view(torch.int16))
+    log(f"split entry points H={H} L={L} r={r}: identical ({H * G} blocks)")
