@@ -194,7 +194,24 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         if (key[i] >= 0 && bucket(key[i]) == bin) cand[pos_c++] = key[i];
     __syncthreads();
     int32_t T = 0;
-    if (n1 <= 1024) {
+    if (n1 <= 64) {
+        // few candidates: lane i of wave 0 takes candidate i and counts the
+        // larger and the equal ones; T is a candidate with #(> T) < need <= #(>= T)
+        if (wave == 0) {
+            const int32_t mine = lane < (int)n1 ? cand[lane] : -1;
+            uint32_t gt = 0, ge = 0;
+            for (uint32_t i = 0; i < n1; ++i) {
+                const int32_t x = cand[i];
+                gt += x > mine;
+                ge += x >= mine;
+            }
+            const uint64_t hit = __ballot(lane < (int)n1 && gt < need && need <= ge);
+            const int32_t t = __shfl(mine, __builtin_ctzll(hit), 64);   // whole wave active
+            if (lane == 0) s_T = t;
+        }
+        __syncthreads();
+        T = s_T;
+    } else if (n1 <= 1024) {
         // one wave, candidates held in registers (16 slots of 64)
         if (wave == 0) {
             int32_t c[16];
