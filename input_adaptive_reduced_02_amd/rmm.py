@@ -15,7 +15,8 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librmm.so")
+# the library built in-tree; RMM_LIB selects another build of it
+LIB_PATH = os.environ.get("RMM_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "librmm.so")
 
 RMM_OK, RMM_EINVAL, RMM_EUNSUPPORTED, RMM_EHIP = 0, -1, -2, -3
 RMM_F32, RMM_BF16 = 0, 1
