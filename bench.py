@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--headline-r", type=float, default=0.5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-groups", type=int, default=None, help="row groups the oracle baseline runs")
+    p.add_argument("--error-study", action="store_true",
+                   help="instead of timing: relative Frobenius error of the reduced product against the r = 1 "
+                        "product, for the product score, the activation-only score and random retention")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before the workload, copy a MIB-MiB buffer 5 times (reference kernel for HBM counters)")
     return p.parse_args()
@@ -312,6 +315,55 @@ def copy_calibration(torch, mib, dev):
     del src, dst
 
 
+def error_study(torch, dev):
+    """Selection quality on the synthetic linear workloads: for every r < 1,
+    ||Y_r - Y_1||_F / ||Y_1||_F with Y_1 the r = 1 product, for the product score
+    (with B norms), the pages' activation-only score, and a seeded uniformly
+    random kept set of the same size (the pages' random-pruning baseline).
+    Every product runs through the hot-path kernels with binary32 outputs; the
+    product rule also reports its Frobenius bound sqrt(sum_g beta_g^2) relative
+    to ||Y_1||_F."""
+    import numpy as np
+    rows = []
+    for name in ("attn_proj", "mlp_down", "decode"):
+        W = Linear(name, dev)
+        rmm = W.rmm
+        M, K, gr = W.M, W.K, W.gr
+        G = -(-M // gr)
+        Y1 = rmm.rmm_gemm(W.A, W.B, None, K, gr, ydt=torch.float32).double()
+        n1 = torch.linalg.norm(Y1).item()
+        rng = np.random.default_rng(0)
+        for r in [x for x in W.ratios if x < 1.0]:
+            kk = rmm.rmm_kk(r, K)
+            kpad = rmm.rmm_kk_pad(kk)
+            for rule in ("product", "activation_only", "random"):
+                bound = None
+                if rule == "product":
+                    bound = torch.empty(G, dtype=torch.float64, device=dev)
+                    idx = rmm.rmm_select(W.A, r, gr, bnorm=W.bnorm, bound=bound)
+                elif rule == "activation_only":
+                    idx = rmm.rmm_select(W.A, r, gr)
+                else:
+                    ix = np.empty((G, kpad), np.int32)
+                    for g in range(G):
+                        ix[g, :kk] = np.sort(rng.choice(K, kk, replace=False))
+                        ix[g, kk:] = ix[g, kk - 1]
+                    idx = torch.from_numpy(ix).to(dev)
+                Ap, _ = rmm.rmm_gather(W.A, idx, kk, gr)
+                Y = rmm.rmm_gemm(Ap, W.B, idx, kk, gr, ydt=torch.float32).double()
+                row = dict(workload=name, r=r, kk=kk, rule=rule,
+                           rel_frob=round(torch.linalg.norm(Y - Y1).item() / n1, 6))
+                if bound is not None:
+                    row["rel_bound"] = round(torch.sqrt((bound ** 2).sum()).item() / n1, 6)
+                rows.append(row)
+                log(f"[study] {name} r={r} {rule}: {row['rel_frob']}" +
+                    (f" (bound {row['rel_bound']})" if bound is not None else ""))
+        del W
+        torch.cuda.empty_cache()
+    print(json.dumps({"study": "selection_error", "data": "synthetic",
+                      "unit": "relative Frobenius error against the r = 1 product", "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -324,6 +376,9 @@ def main():
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
         sys.exit(2)
     dev = "cuda:0"
+    if args.error_study:
+        error_study(torch, dev)
+        return
     if args.copy_calibration > 0:
         copy_calibration(torch, args.copy_calibration, dev)
     if args.workload in ("pv4k", "pv16k"):

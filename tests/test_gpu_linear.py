@@ -263,3 +263,34 @@ def test_select_many_groups(case):
     rmm.rmm_select(A, r, gr, bnorm=bnorm, idx=idx, scores=scores, thresh=thresh, bound=bound)
     check_index_range(idx, K)
     check_selection(c, r, gr, bnorm, idx, scores, thresh, bound, tag)
+
+
+@pytest.mark.parametrize("workload,r", [("attn_proj", 0.5), ("decode", 0.3)], ids=lambda x: str(x))
+def test_full_size_activation_only(workload, r):
+    """The pages' activation-only rule (score = ||A[rows_g, k]||_2, no B norms)
+    at full size: every group's scores and kept set against the oracle's
+    activation-only selection, sampled output rows element by element."""
+    c = _full(workload)
+    M, K = c["A"].shape
+    N = c["B"].shape[1]
+    gr = synth.GROUP_ROWS[workload]
+    tag = f"{workload} activation-only r={r}"
+    log(f"full {tag}")
+    kk = rmm.rmm_kk(r, K)
+    G = -(-M // gr)
+    scores = torch.empty((G, K), dtype=torch.float32, device=DEV)
+    idx = torch.zeros((G, rmm.rmm_kk_pad(kk)), dtype=torch.int32, device=DEV)
+    rmm.rmm_select(c["A"], r, gr, idx=idx, scores=scores)
+    check_index_range(idx, K)
+    sel = O.select(c["A64"], r, gr, None)
+    assert np.array_equal(down(scores), sel["s32"]), f"{tag}: scores differ from the oracle"
+    ig = down(idx)
+    for g in range(G):
+        compare_sets(ig[g], sel, g, kk, tag)
+    Ap, _ = rmm.rmm_gather(c["A"], idx, kk, gr)
+    Y = rmm.rmm_gemm(Ap, c["B"], idx, kk, gr)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(12).integers(0, M, G)]))
+    Yref = np.stack([O.reduced(c["A64"], c["B64"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
+    Sabs = np.stack([O.reduced(c["A64abs"], c["B64abs"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
+    check_output(widen(Y)[rows], Yref, Sabs, kk, tag + f" ({len(rows)} rows)")
