@@ -246,6 +246,33 @@ k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
     }
     vmwait<0>();   // the trailing index loads
 
+    if (ydt == 1) {
+        // bf16 output: stage the tile in LDS (the ring is free once every wave
+        // has passed the barrier below), then write whole 16-byte row chunks
+        // (N % 8 == 0, so a chunk never crosses N)
+        constexpr int PITCH = TN * 2 + 16;   // bytes per staged row; +16 spreads rows over the banks
+        static_assert(TM * PITCH <= S::NSTAGE * S::STAGE_ELEMS * 2, "staged tile fits the ring");
+        char *st = (char *)smem;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = wm * WM + fm * 32 + acc_row(lane, v), c = wn * WN + fn * 32 + acc_col(lane);
+                    *(uint16_t *)(st + r * PITCH + 2 * c) = (uint16_t)f32_to_bf16(acc[fm][fn][v]);
+                }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int e = threadIdx.x; e < TM * (TN / 8); e += NT) {
+            const int r = e / (TN / 8), ch = e % (TN / 8);
+            const int64_t row = row0 + r, col = col0 + 8 * ch;
+            if (row < row_end && col < N)
+                *(uint4 *)((uint16_t *)Y + row * ldy + col) = *(const uint4 *)(st + r * PITCH + 16 * ch);
+        }
+        return;
+    }
+
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll

@@ -206,6 +206,30 @@ k_pv_gemm(const uint16_t *__restrict__ Pt, const uint16_t *__restrict__ V, int64
     }
     pv_vmwait<0>();   // the trailing reloads: no DMA may land after the workgroup ends
 
+    if (odt == 1) {
+        // bf16 output: stage the 128 x 128 tile in LDS (the ring is free once
+        // every wave has passed the barrier below), then write 16-byte row chunks
+        constexpr int PITCH = 128 * 2 + 16;
+        char *st = (char *)smem;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = wm * 64 + fm * 32 + acc_row(lane, v), c = wn * 64 + fn * 32 + acc_col(lane);
+                    *(uint16_t *)(st + r * PITCH + 2 * c) = (uint16_t)f32_to_bf16(acc[fm][fn][v]);
+                }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int e = threadIdx.x; e < 128 * 16; e += 256) {
+            const int r = e >> 4, ch = e & 15;
+            if (r < nq)
+                *(uint4 *)((uint16_t *)O + (h * L + q0 + r) * 128 + 8 * ch) = *(const uint4 *)(st + r * PITCH + 16 * ch);
+        }
+        return;
+    }
+
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
