@@ -44,6 +44,7 @@ _D = ctypes.POINTER(ctypes.c_double)
 _F = ctypes.POINTER(ctypes.c_float)
 _I32 = ctypes.POINTER(ctypes.c_int32)
 _I64 = ctypes.POINTER(ctypes.c_int64)
+_I8 = ctypes.POINTER(ctypes.c_int8)
 _L = ctypes.c_int64
 
 
@@ -72,6 +73,12 @@ def _declare(lib):
     lib.oracle_pv_block.argtypes = [_D, _L, _L, _D, _L, _I32, _L, _D]
     lib.oracle_pv_bound.restype = ctypes.c_double
     lib.oracle_pv_bound.argtypes = [_D, _L, _L, _D, _L, _L, _I32, _L]
+    lib.oracle_quantize_q8.restype = None
+    lib.oracle_quantize_q8.argtypes = [_F, _L, _L, _L, _I8, _L, _F]
+    lib.oracle_dequant_q8.restype = None
+    lib.oracle_dequant_q8.argtypes = [_I8, _L, _F, _L, _L, _D, _L]
+    lib.oracle_rownorms_q8.restype = None
+    lib.oracle_rownorms_q8.argtypes = [_I8, _L, _F, _L, _L, _D]
 
 
 def _p(a, typ):
@@ -287,8 +294,44 @@ def pv_select_block(Pt, V, L, qblock, g, r, causal=True, lib=None):
                 near=near_ties(s64, s32, idx))
 
 
+# ---------------------------------------------------------------- int8 weights
+def quantize_q8(B, lib=None):
+    """(q int8 [K, N], scale float32 [N]) of a weight given as binary32 values
+    (bf16 weights widened exactly), reading R7."""
+    lib = lib or load()
+    B = np.ascontiguousarray(B, dtype=np.float32)
+    K, N = B.shape
+    q = np.empty((K, N), np.int8)
+    s = np.empty(N, np.float32)
+    lib.oracle_quantize_q8(_p(B, _F), K, N, N, _p(q, _I8), N, _p(s, _F))
+    return q, s
+
+
+def dequant_q8(q, scale, lib=None):
+    """The dequantised weight scale[n] * q[k, n] as float64 (exact)."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(scale, dtype=np.float32)
+    K, N = q.shape
+    Bd = np.empty((K, N), np.float64)
+    lib.oracle_dequant_q8(_p(q, _I8), N, _p(s, _F), K, N, _p(Bd, _D), N)
+    return Bd
+
+
+def rownorms_q8(q, scale, lib=None):
+    """Row norms of the dequantised weight, float64 [K]."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(scale, dtype=np.float32)
+    K, N = q.shape
+    b = np.empty(K, np.float64)
+    lib.oracle_rownorms_q8(_p(q, _I8), N, _p(s, _F), K, N, _p(b, _D))
+    return b
+
+
 __all__ = [
     "load", "widen_bf16", "widen_f32", "kk", "rownorms", "colnorms", "scores", "topk", "select",
     "reduced", "reduced_entries", "dense", "bound", "pv_prefix", "pv_block_inputs", "pv_scores",
     "pv_block", "pv_bound", "pv_select_block", "near_ties", "NEAR_TIE_REL",
+    "quantize_q8", "dequant_q8", "rownorms_q8",
 ]

@@ -41,6 +41,15 @@
  *      k < K_g = min(L, qblock*(g+1)); the score of key k is
  *      (sum over the block's queries of P[q,k]) * ||V[k,:]||_2; k_g = kk(r, K_g).
  *   R6 every sum runs in ascending index order.
+ *   R7 int8 weights ("Resultados Experimentais", item "Compatibilidade":
+ *      the method works on INT8-quantised weights; the pages fix no scheme).
+ *      Symmetric absmax quantisation with one binary32 scale per output
+ *      column n: s_n = max_k |B[k,n]| / 127, q[k,n] = round-half-even(B[k,n]
+ *      / s_n) clamped to [-127, 127] (s_n = 0 and q = 0 for an all-zero
+ *      column), both divisions in binary32 because they decide integers.  The
+ *      method then runs on the dequantised weight s_n * q[k,n] (exact in
+ *      binary64): its row norms score the slices and its kept rows are
+ *      multiplied.
  */
 #include <math.h>
 #include <stdint.h>
@@ -282,4 +291,58 @@ double oracle_pv_bound(const double *Ptb, int64_t ldp, int64_t nq, const double 
     }
     free(kept);
     return beta;
+}
+
+/* ---- int8 weight quantisation, reading R7.  B is K x N binary32 (row stride
+ * ldb); writes q (row stride ldq) and one scale per column. */
+void oracle_quantize_q8(const float *B, int64_t K, int64_t N, int64_t ldb, int8_t *q, int64_t ldq,
+                        float *scale)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(B[k * ldb + n]);
+            if (a > amax)
+                amax = a;
+        }
+        float s = amax / 127.0f;
+        scale[n] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            if (s == 0.0f) {
+                q[k * ldq + n] = 0;
+                continue;
+            }
+            float t = rintf(B[k * ldb + n] / s);
+            if (t > 127.0f)
+                t = 127.0f;
+            if (t < -127.0f)
+                t = -127.0f;
+            q[k * ldq + n] = (int8_t)t;
+        }
+    }
+}
+
+/* ---- the dequantised weight of reading R7: Bd[k][n] = s_n * q[k][n], exact
+ * in binary64 (a 24-bit by 8-bit product). */
+void oracle_dequant_q8(const int8_t *q, int64_t ldq, const float *scale, int64_t K, int64_t N,
+                       double *Bd, int64_t ldd)
+{
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            Bd[k * ldd + n] = (double)scale[n] * (double)q[k * ldq + n];
+}
+
+/* ---- row norms of the dequantised weight (reading R7 with R1):
+ * b[k] = ||(s_n q[k][n])_n||_2, ascending n. */
+void oracle_rownorms_q8(const int8_t *q, int64_t ldq, const float *scale, int64_t K, int64_t N,
+                        double *b)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double v = (double)scale[n] * (double)q[k * ldq + n];
+            acc += v * v;
+        }
+        b[k] = sqrt(acc);
+    }
 }

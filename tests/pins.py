@@ -388,9 +388,76 @@ def pin_pv_hand(lib):
         assert np.array_equal(Ob, np.array(blk["O"], float))
 
 
+# ------------------------------------------------------------------ int8 weights
+def pin_q8_hand(lib):
+    """The hand-worked quantisation of tests/golden/hand_q8.txt; the dequantised
+    values and row norms checked in exact rational arithmetic."""
+    g = read_golden("hand_q8.txt")
+    B = np.array(g["B"], np.float32)
+    q, s = O.quantize_q8(B, lib)
+    assert q.tolist() == g["q"], q
+    assert s.view(np.uint32).tolist() == g["scale_bits"]
+    Bd = O.dequant_q8(q, s, lib)
+    b = O.rownorms_q8(q, s, lib)
+    for k in range(B.shape[0]):
+        ss = Fraction(0)
+        for n in range(B.shape[1]):
+            v = Fraction(float(s[n])) * int(q[k, n])
+            assert Fraction(float(Bd[k, n])) == v
+            ss += v * v
+        assert abs(Fraction(float(b[k])) ** 2 - ss) <= ss * Fraction(1, 10 ** 15)
+
+
+def pin_q8_rounding(lib):
+    """Scales equal numpy's binary32 division of the column absmax by 127; every
+    code is the integer nearest to B/s (exact halves to even), within [-127, 127],
+    +-127 at each column's absmax; all-zero columns give s = 0, q = 0."""
+    rng = _rng(21)
+    K, N = 37, 29
+    B = (rng.standard_normal((K, N)) * rng.lognormal(0, 1, N)[None, :] * 0.02).astype(np.float32)
+    B[:, 4] = 0.0
+    B[:, 7] = 0.0
+    B[3, 7] = -2.5
+    # a column whose scale is exactly 2^-4, with exact halves in B/s
+    B[:, 10] = np.array([(k - 18) * 0.5 * 2.0 ** -4 for k in range(K)], np.float32)
+    B[0, 10] = 127 * 2.0 ** -4
+    q, s = O.quantize_q8(B, lib)
+    amax = np.abs(B).max(axis=0)
+    want_s = (amax / np.float32(127)).astype(np.float32)
+    assert np.array_equal(s.view(np.uint32), want_s.view(np.uint32))
+    assert s[10] == 2.0 ** -4
+    assert np.all(q[:, 4] == 0) and s[4] == 0
+    assert q[3, 7] == -127 and np.count_nonzero(q[:, 7]) == 1
+    assert np.all(np.abs(q.astype(int)) <= 127)
+    nz = s > 0
+    x = B[:, nz].astype(np.float64) / s[nz].astype(np.float64)
+    qn = q[:, nz].astype(np.float64)
+    assert np.all(np.abs(x - qn) <= 0.5 + 1e-6)
+    far = np.abs(np.abs(x - np.floor(x)) - 0.5) > 1e-5
+    assert np.array_equal(qn[far], np.rint(x)[far])
+    assert np.array_equal(q[:, 10].astype(np.float64), np.rint(B[:, 10] / 2.0 ** -4))
+    am = np.argmax(np.abs(B), axis=0)
+    assert np.all(np.abs(q[am[nz], np.flatnonzero(nz)].astype(int)) == 127)
+
+
+def pin_q8_dequant_norms(lib):
+    """Dequantised weight = numpy's float64 product scale[n] * q[k, n]; its
+    error is at most half a step per element; row norms = numpy's norms."""
+    rng = _rng(22)
+    K, N = 45, 33
+    B = (rng.standard_normal((K, N)) * rng.lognormal(0, 1, N)[None, :] * 0.02).astype(np.float32)
+    q, s = O.quantize_q8(B, lib)
+    Bd = O.dequant_q8(q, s, lib)
+    want = s.astype(np.float64)[None, :] * q.astype(np.float64)
+    assert np.array_equal(Bd, want)
+    assert np.all(np.abs(B.astype(np.float64) - Bd) <= 0.5 * s.astype(np.float64)[None, :] * (1 + 1e-6))
+    b = O.rownorms_q8(q, s, lib)
+    assert np.allclose(b, np.linalg.norm(want, axis=1), rtol=1e-13, atol=0)
+
+
 ALL_PINS = [
     pin_kk_exact_rational, pin_kk_golden, pin_norms_numpy, pin_scores_numpy, pin_topk_argsort,
     pin_topk_invariants, pin_topk_bruteforce, pin_select_nesting, pin_reduced_numpy,
     pin_dense_numpy, pin_reduced_exact, pin_bound, pin_closed_forms, pin_hand_examples,
-    pin_pv_numpy, pin_pv_hand,
+    pin_pv_numpy, pin_pv_hand, pin_q8_hand, pin_q8_rounding, pin_q8_dequant_norms,
 ]

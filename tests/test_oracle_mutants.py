@@ -44,6 +44,12 @@ MUTANTS = [
     ("pv_score_without_vnorm", "void oracle_pv_scores", [("double s = mass * sqrt(vv);", "double s = mass;")]),
     ("pv_block_transposed_P", "void oracle_pv_block", [("double p = Ptb[k * ldp + i];", "double p = Ptb[(i % nq) * ldp + (k % nq)];")]),
     ("pv_bound_mass_not_l2", "double oracle_pv_bound", [("pp += p * p;", "pp += p;")]),
+    ("q8_floor", "void oracle_quantize_q8", [("rintf(B[k * ldb + n] / s)", "floorf(B[k * ldb + n] / s)")]),
+    ("q8_ties_away", "void oracle_quantize_q8", [("rintf(B[k * ldb + n] / s)", "roundf(B[k * ldb + n] / s)")]),
+    ("q8_scale_sum", "void oracle_quantize_q8", [("if (a > amax)\n                amax = a;", "amax += a;")]),
+    ("q8_scale_128", "void oracle_quantize_q8", [("amax / 127.0f", "amax / 128.0f")]),
+    ("q8_dequant_row_scale", "void oracle_dequant_q8", [("(double)scale[n]", "(double)scale[k % N]")]),
+    ("q8_rownorm_no_scale", "void oracle_rownorms_q8", [("(double)scale[n] * (double)q", "(double)q")]),
 ]
 
 
