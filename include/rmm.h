@@ -203,6 +203,42 @@ int rmm_pv_gemm(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int
                 int64_t qblock, int causal, const int32_t *idx, int64_t ldidx, void *O, int odt,
                 void *stream);
 
+/* ---- int8 weights.  The pages ("Resultados Experimentais", item
+ * "Compatibilidade") state that the method works on INT8-quantised weights
+ * and fix no scheme.  Format used here: Bq [K][ldq] int8 codes and one
+ * binary32 scale per output column,
+ *   scale[n] = max_k |B[k][n]| / 127,   Bq[k][n] = round-half-even(B[k][n] / scale[n]),
+ * both divisions correctly rounded in binary32, codes in [-127, 127]; an
+ * all-zero column has scale 0 and codes 0.  The method runs on the
+ * dequantised weight scale[n] * Bq[k][n]: rmm_rownorms_q8 gives its row norms
+ * (the B norms rmm_select takes), rmm_gemm_q8 multiplies its kept rows, read
+ * as int8 (half the bytes of a bf16 row).  The activation side (score,
+ * select, gather) is unchanged.  Layout rules: N % 16 == 0, ldq % 16 == 0,
+ * Bq 16-byte aligned, scale 4-byte aligned.
+ *
+ * rmm_quantize_q8: quantise a bf16 weight B [K][ldb] (finite values) into Bq
+ * and scale [N].  Runs once per weight; `scale` doubles as the column-maximum
+ * accumulator while it runs. */
+int rmm_quantize_q8(const uint16_t *B, int64_t K, int64_t N, int64_t ldb, int8_t *Bq, int64_t ldq,
+                    float *scale, void *stream);
+
+/* Row norms of the dequantised weight, binary64 [K]:
+ *   bnorm[k] = sqrt(sum_n (scale[n] * Bq[k][n])^2), each term exact, the sum
+ * taken in ascending n with one rounding per square and per addition. */
+int rmm_rownorms_q8(const int8_t *Bq, int64_t ldq, const float *scale, int64_t K, int64_t N,
+                    double *bnorm, void *stream);
+
+/* The reduced product on an int8 weight:
+ *   Y[m][n] = scale[n] * sum_{j < kk} A[m][j] * Bq[row(g, j)][n],
+ * g and row(g, j) as rmm_gemm (idx == NULL: row j, the dense product when
+ * kk == K).  A is the bf16 panel of rmm_gemm.  Each product of a bf16 value
+ * and a code is exact in fp32; fp32 accumulation, ascending j within each
+ * 64-deep slab; the scale multiplies the fp32 sum once; Y as rmm_gemm.
+ * No workspace.  Errors: RMM_EINVAL for bad pointers/sizes. */
+int rmm_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq, const float *scale,
+                const int32_t *idx, int64_t ldidx, int64_t M, int64_t N, int64_t kk, int64_t group_rows,
+                void *Y, int ydt, int64_t ldy, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

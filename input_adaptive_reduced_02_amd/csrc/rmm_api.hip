@@ -153,6 +153,40 @@ int rmm_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, con
                                   as_stream(stream)));
 }
 
+int rmm_quantize_q8(const uint16_t *B, int64_t K, int64_t N, int64_t ldb, int8_t *Bq, int64_t ldq,
+                    float *scale, void *stream)
+{
+    if (K < 1 || !ok_matrix(B, RMM_BF16, N, ldb) || N % 16 != 0) return RMM_EINVAL;
+    if (!Bq || !aligned16(Bq) || ldq < N || ldq % 16 != 0 || !scale || !aligned4(scale)) return RMM_EINVAL;
+    if (K > INT32_MAX || K * (N / 16) > (int64_t)INT32_MAX * 256) return RMM_EUNSUPPORTED;
+    return hip_status(launch_quantize_q8(B, K, N, ldb, Bq, ldq, scale, as_stream(stream)));
+}
+
+int rmm_rownorms_q8(const int8_t *Bq, int64_t ldq, const float *scale, int64_t K, int64_t N,
+                    double *bnorm, void *stream)
+{
+    if (K < 1 || N < 1 || N % 16 != 0 || !Bq || !aligned16(Bq) || ldq < N || ldq % 16 != 0) return RMM_EINVAL;
+    if (!scale || !aligned4(scale) || !bnorm || !aligned8(bnorm)) return RMM_EINVAL;
+    return hip_status(launch_rownorms_q8(Bq, ldq, scale, K, N, bnorm, as_stream(stream)));
+}
+
+int rmm_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq, const float *scale,
+                const int32_t *idx, int64_t ldidx, int64_t M, int64_t N, int64_t kk, int64_t group_rows,
+                void *Y, int ydt, int64_t ldy, void *stream)
+{
+    if (M < 1 || N < 1 || kk < 1 || group_rows < 1) return RMM_EINVAL;
+    if (!ok_matrix(A, RMM_BF16, kk, lda)) return RMM_EINVAL;
+    if (!Bq || !aligned16(Bq) || N % 16 != 0 || ldq < N || ldq % 16 != 0) return RMM_EINVAL;
+    if (!scale || !aligned4(scale)) return RMM_EINVAL;
+    if (idx && (!aligned16(idx) || ldidx < kk || ldidx % 4 != 0)) return RMM_EINVAL;
+    if (!ok_matrix(Y, ydt, N, ldy)) return RMM_EINVAL;
+    if (kk > INT32_MAX || (M + group_rows - 1) / group_rows > INT32_MAX / 64 ||
+        (double)((M + group_rows - 1) / group_rows) * ((group_rows + 63) / 64) * ((N + 127) / 128) > INT32_MAX / 2)
+        return RMM_EUNSUPPORTED;
+    return hip_status(launch_gemm_q8(A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy,
+                                     as_stream(stream)));
+}
+
 size_t rmm_attn_pv_workspace_bytes(int64_t H, int64_t L, int64_t D, double r, int64_t qblock,
                                    int causal, int have_idx_out, int have_scores_out)
 {

@@ -75,6 +75,12 @@ def _declare(L):
     L.rmm_pv_select.argtypes = [_P, _P, _L, _L, _L, _Dbl, _L, _I, _P, _L, _P, _P, _S, _P]
     L.rmm_pv_gemm.restype = _I
     L.rmm_pv_gemm.argtypes = [_P, _P, _L, _L, _L, _Dbl, _L, _I, _P, _L, _P, _I, _P]
+    L.rmm_quantize_q8.restype = _I
+    L.rmm_quantize_q8.argtypes = [_P, _L, _L, _L, _P, _L, _P, _P]
+    L.rmm_rownorms_q8.restype = _I
+    L.rmm_rownorms_q8.argtypes = [_P, _L, _P, _L, _L, _P, _P]
+    L.rmm_gemm_q8.restype = _I
+    L.rmm_gemm_q8.argtypes = [_P, _L, _P, _L, _P, _P, _L, _L, _L, _L, _L, _P, _I, _L, _P]
     return L
 
 
@@ -245,6 +251,53 @@ def rmm_pv_gemm(Pt, V, r, idx=None, qblock=128, causal=True, O=None, odt=torch.b
         _ptr(Pt), _ptr(V), H, L, D, float(r), qblock, int(bool(causal)), _ptr(idx), ldix, _ptr(O), _dt(O),
         _stream(V)))
     return O
+
+
+def rmm_quantize_q8(B, Bq=None, scale=None):
+    """(Bq int8 [K, N], scale float32 [N]) of a bf16 weight B [K, N]."""
+    K, N = B.shape
+    if Bq is None:
+        Bq = torch.empty((K, N), dtype=torch.int8, device=B.device)
+    if scale is None:
+        scale = torch.empty(N, dtype=torch.float32, device=B.device)
+    _check("rmm_quantize_q8", lib().rmm_quantize_q8(_ptr(B), K, N, _ld(B), _ptr(Bq), _ld(Bq), _ptr(scale),
+                                                     _stream(B)))
+    return Bq, scale
+
+
+def rmm_rownorms_q8(Bq, scale, bnorm=None):
+    """Row norms of the dequantised int8 weight, binary64 [K]."""
+    K, N = Bq.shape
+    if bnorm is None:
+        bnorm = torch.empty(K, dtype=torch.float64, device=Bq.device)
+    _check("rmm_rownorms_q8", lib().rmm_rownorms_q8(_ptr(Bq), _ld(Bq), _ptr(scale), K, N, _ptr(bnorm),
+                                                     _stream(Bq)))
+    return bnorm
+
+
+def rmm_gemm_q8(A, Bq, scale, idx, kk, group_rows, Y=None, ydt=torch.bfloat16, M=None):
+    """Y = scale * (A[:, :kk] * Bq[rows, :]) per group, rows as rmm_gemm."""
+    M = A.shape[0] if M is None else M
+    N = Bq.shape[1]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=ydt, device=A.device)
+    _check("rmm_gemm_q8", lib().rmm_gemm_q8(
+        _ptr(A), _ld(A), _ptr(Bq), _ld(Bq), _ptr(scale), _ptr(idx), _ld(idx) if idx is not None else 0, M, N,
+        kk, group_rows, _ptr(Y), _dt(Y), _ld(Y), _stream(A)))
+    return Y
+
+
+def linear_q8(A, Bq, scale, r, group_rows, bnorm, ydt=torch.bfloat16):
+    """The linear-layer chain on an int8 weight: select (with the dequantised
+    weight's row norms `bnorm`) -> gather -> reduced int8 GEMM; r == 1 runs
+    the same GEMM on A in place."""
+    M, K = A.shape
+    kk = rmm_kk(r, K)
+    if kk == K:
+        return rmm_gemm_q8(A, Bq, scale, None, K, group_rows, ydt=ydt)
+    idx = rmm_select(A, r, group_rows, bnorm=bnorm)
+    Ap, _ = rmm_gather(A, idx, kk, group_rows)
+    return rmm_gemm_q8(Ap, Bq, scale, idx, kk, group_rows, ydt=ydt)
 
 
 def linear(A, B, r, group_rows, bnorm=None, ydt=torch.bfloat16, activation_only=False):

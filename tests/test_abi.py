@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -164,3 +164,21 @@ def test_validation_rejects_bad_arguments():
     assert L.rmm_pv_gemm(P, P2, 1, 256, 128, 0.5, 128, 1, P, 100, P3, BF, None) == EINVAL  # ldidx
     assert L.rmm_pv_gemm(P, P2, 1, 256, 128, 0.5, 128, 1, None, 0, None, BF, None) == EINVAL  # no O
     assert L.rmm_pv_gemm(P, P2, 1, 100, 128, 1.0, 128, 1, None, 0, P3, BF, None) == EUNSUP  # L % 8
+    # quantize_q8(B, K, N, ldb, Bq, ldq, scale, stream)
+    assert L.rmm_quantize_q8(P, 4, 24, 24, P2, 32, P3, None) == EINVAL      # N % 16
+    assert L.rmm_quantize_q8(P, 0, 32, 32, P2, 32, P3, None) == EINVAL      # K < 1
+    assert L.rmm_quantize_q8(P, 4, 32, 32, P2, 24, P3, None) == EINVAL      # ldq < N
+    assert L.rmm_quantize_q8(P, 4, 32, 32, P2, 40, P3, None) == EINVAL      # ldq % 16
+    assert L.rmm_quantize_q8(P, 4, 32, 32, MIS, 32, P3, None) == EINVAL
+    assert L.rmm_quantize_q8(P, 4, 32, 32, P2, 32, None, None) == EINVAL
+    # rownorms_q8(Bq, ldq, scale, K, N, bnorm, stream)
+    assert L.rmm_rownorms_q8(P, 32, P2, 4, 24, P3, None) == EINVAL          # N % 16
+    assert L.rmm_rownorms_q8(P, 32, None, 4, 32, P3, None) == EINVAL
+    assert L.rmm_rownorms_q8(P, 32, P2, 4, 32, ctypes.c_void_p((3 << 20) + 4), None) == EINVAL
+    # gemm_q8(A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk, gr, Y, ydt, ldy, stream)
+    assert L.rmm_gemm_q8(P, 64, P2, 32, P3, None, 0, 64, 24, 64, 64, P3, BF, 24, None) == EINVAL   # N % 16
+    assert L.rmm_gemm_q8(P, 64, P2, 32, None, None, 0, 64, 32, 64, 64, P3, BF, 32, None) == EINVAL  # no scale
+    assert L.rmm_gemm_q8(P, 32, P2, 32, P3, None, 0, 64, 32, 64, 64, P3, BF, 32, None) == EINVAL    # lda < kk
+    assert L.rmm_gemm_q8(P, 64, P2, 32, P3, P, 32, 64, 32, 64, 64, P3, BF, 32, None) == EINVAL      # ldidx < kk
+    assert L.rmm_gemm_q8(P, 64, P2, 40, P3, None, 0, 64, 32, 64, 64, P3, BF, 32, None) == EINVAL    # ldq % 16
+    assert L.rmm_gemm_q8(P, 64, P2, 32, P3, None, 0, 64, 32, 64, 64, P3, 5, 32, None) == EINVAL     # ydt
