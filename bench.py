@@ -12,7 +12,8 @@ lognormal channel scales, 1% outlier channels x20) times W 4096x4096 bf16
 `value` is the retained-K TFLOP/s of the whole step at r = 0.5
 (2*M*kk*N / step time); per-r stage times, GEMM-only TFLOP/s and the speed-ups
 over r = 1.0 are reported beside it.  Other workloads (--workload mlp_down,
-decode, pv4k, pv16k, tiny) use the same contract.
+decode, decode_q8, pv4k, pv16k, tiny) use the same contract; decode_q8 is the
+decode shape on the int8 weight path (weights quantised once, before timing).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -41,7 +42,7 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="attn_proj",
-                   choices=["attn_proj", "mlp_down", "decode", "pv4k", "pv16k", "tiny"])
+                   choices=["attn_proj", "mlp_down", "decode", "decode_q8", "pv4k", "pv16k", "tiny"])
     p.add_argument("--ratios", type=str, default=None, help="comma-separated r values")
     p.add_argument("--headline-r", type=float, default=0.5)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -56,7 +57,8 @@ def parse():
 
 # ------------------------------------------------------------------ workloads
 class Linear:
-    """X [M,K] times W [K,N] with per-group selection (attn_proj, mlp_down, decode, tiny)."""
+    """X [M,K] times W [K,N] with per-group selection (attn_proj, mlp_down, decode, tiny;
+    decode_q8: the decode inputs with the weight quantised to int8)."""
 
     def __init__(self, name, dev):
         import numpy as np
@@ -64,11 +66,13 @@ class Linear:
         from input_adaptive_reduced_02_amd import rmm, synth
         self.rmm, self.torch, self.np = rmm, torch, np
         self.name = name
-        self.M, self.K, self.N = synth.FULL_SHAPES[name]
-        self.gr = synth.GROUP_ROWS[name]
-        self.ratios = synth.RATIOS[name]
+        self.q8 = name == "decode_q8"
+        base = "decode" if self.q8 else name
+        self.M, self.K, self.N = synth.FULL_SHAPES[base]
+        self.gr = synth.GROUP_ROWS[base]
+        self.ratios = synth.RATIOS[base]
         t0 = time.time()
-        d = synth.linear_inputs(name)
+        d = synth.linear_inputs(base)
         self.host = d
         if d["dtype"] == "bf16":
             self.A = torch.from_numpy(d["A"].view(np.int16)).view(torch.bfloat16).to(dev)
@@ -77,11 +81,20 @@ class Linear:
             self.A = torch.from_numpy(d["A"]).to(dev)
             self.B = torch.from_numpy(d["B"]).to(dev)
         self.f32 = d["dtype"] == "f32"
-        self.bnorm = rmm.rmm_rownorms(self.B)   # once per weight, outside the timed step
-        # The decode weight's kept rows (141-470 MB) are the size of the
-        # 256 MB last-level cache; steps rotate over 3 copies of the weight so
-        # that every step streams it from HBM, as a real decode step would.
-        self.Bs = [self.B] + [self.B.clone() for _ in range(2 if name == "decode" else 0)]
+        # per-weight work, outside the timed step: B row norms (and for int8
+        # weights the quantisation and the norms of the dequantised weight)
+        if self.q8:
+            self.B, self.scale = rmm.rmm_quantize_q8(self.B)
+            self.bnorm = rmm.rmm_rownorms_q8(self.B, self.scale)
+        else:
+            self.bnorm = rmm.rmm_rownorms(self.B)
+        # The decode weight's kept rows (70-470 MB) are the size of the 256 MB
+        # last-level cache; steps rotate over copies of the weight (3 of the
+        # bf16 weight, 8 of the int8 one) so that between two reads of one copy
+        # at least 280 MB of other weight rows stream by, and every step reads
+        # its weight from HBM, as a real decode step would.
+        copies = {"decode": 3, "decode_q8": 8}.get(name, 1)
+        self.Bs = [self.B] + [self.B.clone() for _ in range(copies - 1)]
         self._rot = 0
         torch.cuda.synchronize()
         log(f"[bench] {name}: inputs {self.M}x{self.K} @ {self.K}x{self.N} ready in {time.time() - t0:.1f}s")
@@ -90,7 +103,8 @@ class Linear:
 
     def describe(self, r):
         dt = "fp32" if self.f32 else "bf16"
-        return (f"{self.name}: X {self.M}x{self.K} {dt} @ W {self.K}x{self.N} {dt}, "
+        wdt = "int8 (one binary32 scale per column)" if self.q8 else dt
+        return (f"{self.name}: X {self.M}x{self.K} {dt} @ W {self.K}x{self.N} {wdt}, "
                 f"{self.gr}-row selection groups, r={r}")
 
     def next_B(self):
@@ -104,6 +118,12 @@ class Linear:
         kk = rmm.rmm_kk(r, self.K)
         self.kk = kk
         Y = torch.empty((self.M, self.N), dtype=torch.float32 if self.f32 else torch.bfloat16, device=self.dev)
+        if self.q8:
+            wq = torch.empty(max(1, rmm.rmm_gemm_q8_workspace_bytes(self.M, self.N, kk, self.gr)),
+                             dtype=torch.uint8, device=self.dev)
+        if self.q8 and kk == self.K:
+            return [("gemm", lambda: rmm.rmm_gemm_q8(self.A, self.next_B(), self.scale, None, kk, self.gr,
+                                                     Y=Y, ws=wq))], kk
         if kk == self.K and not self.f32:
             return [("gemm", lambda: rmm.rmm_gemm(self.A, self.next_B(), None, kk, self.gr, Y=Y))], kk
         kpad = rmm.rmm_kk_pad(kk)
@@ -117,6 +137,11 @@ class Linear:
             return [sel,
                     ("gather", lambda: rmm.rmm_gather(self.A, idx, kk, self.gr, Apanel=Ap, B=self.B, Bpanel=Bp)),
                     ("gemm", lambda: rmm.rmm_gemm(Ap, Bp, None, kk, self.gr, Y=Y))], kk
+        if self.q8:
+            return [sel,
+                    ("gather", lambda: rmm.rmm_gather(self.A, idx, kk, self.gr, Apanel=Ap)),
+                    ("gemm", lambda: rmm.rmm_gemm_q8(Ap, self.next_B(), self.scale, idx, kk, self.gr, Y=Y,
+                                                     ws=wq))], kk
         return [sel,
                 ("gather", lambda: rmm.rmm_gather(self.A, idx, kk, self.gr, Apanel=Ap)),
                 ("gemm", lambda: rmm.rmm_gemm(Ap, self.next_B(), idx, kk, self.gr, Y=Y))], kk
@@ -125,15 +150,17 @@ class Linear:
         return 2.0 * self.M * self.rmm.rmm_kk(r, self.K) * self.N
 
     def gemm_bytes(self, r):
-        """Algorithmic HBM bytes of one reduced-GEMM launch: kept B rows, the A
-        panel (or A), and Y."""
+        """Algorithmic HBM bytes of one reduced-GEMM launch: kept B rows (int8:
+        one byte per weight, plus the column scales), the A panel (or A), and Y."""
         kk = self.rmm.rmm_kk(r, self.K)
         yb = 4 if self.f32 else 2
-        return 2.0 * kk * self.N + 2.0 * self.M * kk + yb * self.M * self.N
+        brow = (1.0 * kk * self.N + 4.0 * self.N) if self.q8 else 2.0 * kk * self.N
+        return brow + 2.0 * self.M * kk + yb * self.M * self.N
 
-    bound = property(lambda self: "hbm" if self.name == "decode" else "mfma")
+    bound = property(lambda self: "hbm" if self.name in ("decode", "decode_q8") else "mfma")
     # the kernel the reduced GEMM runs on (groups of at most 64 rows: the decode kernel)
-    kernel = property(lambda self: "rmm::k_gemm_sk" if self.gr <= 64 else "rmm::k_gemm_dl")
+    kernel = property(lambda self: "rmm::k_gemm_q8" if self.q8 else
+                      ("rmm::k_gemm_sk" if self.gr <= 64 else "rmm::k_gemm_dl"))
 
     def cpu_baseline(self, r, groups):
         """The oracle (single-threaded fp64 C) on `groups` row groups at ratio r:
@@ -144,8 +171,15 @@ class Linear:
         widen = O.widen_f32 if self.f32 else O.widen_bf16
         rows = min(self.M, groups * self.gr)
         A64 = widen(d["A"][:rows])
-        B64 = widen(d["B"])
-        b = O.rownorms(B64)   # per-weight, outside the timed part (as on the GPU)
+        # per-weight work outside the timed part (as on the GPU)
+        if self.q8:
+            from input_adaptive_reduced_02_amd import synth
+            q, s = O.quantize_q8(synth.bf16_bits_to_f32(d["B"]))
+            B64 = O.dequant_q8(q, s)
+            b = O.rownorms_q8(q, s)
+        else:
+            B64 = widen(d["B"])
+            b = O.rownorms(B64)
         t0 = time.perf_counter()
         sel = O.select(A64, r, self.gr, b)
         Y = O.reduced(A64, B64, sel["idx"], sel["kk"], self.gr)
@@ -231,9 +265,12 @@ def torch_int16(torch):
 
 # ------------------------------------------------------------------ timing
 def time_stages(torch, stages, steps, warmup):
-    """Warm up, then time `steps` whole steps (no events inside) and, in a second
-    pass, each stage with events on the launch stream.  Returns (ms_per_step,
-    {stage: mean ms})."""
+    """Warm up, then time `steps` whole steps (no events inside); in a second
+    pass, each stage with events on the launch stream around it; in a third,
+    `steps` launches of the last stage (the GEMM) back to back between two
+    events, which is the kernel's own duration plus the small gap between
+    queued launches (events around a single launch add its launch latency).
+    Returns (ms_per_step, {stage: mean ms}, gemm ms per back-to-back launch)."""
     for _ in range(warmup):
         for _, fn in stages:
             fn()
@@ -259,7 +296,14 @@ def time_stages(torch, stages, steps, warmup):
     per = {}
     for j, (name, _) in enumerate(stages):
         per[name] = sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
-    return ms_step, per
+    gemm = stages[-1][1]
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(steps):
+        gemm()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return ms_step, per, e0.elapsed_time(e1) / steps
 
 
 # ------------------------------------------------------------------ HBM traffic
@@ -267,7 +311,12 @@ def time_stages(torch, stages, steps, warmup):
 GEMM_SOURCES = {
     "linear": ["rmm_gemm.hip", "rmm_gemm_dl.h", "rmm_gemm_sk.h", "rmm_tile.h", "rmm_internal.h"],
     "pv": ["rmm_pv.hip", "rmm_tile.h", "rmm_internal.h"],
+    "q8": ["rmm_q8.hip", "rmm_gemm_dl.h", "rmm_tile.h", "rmm_internal.h"],
 }
+
+
+def source_family(workload):
+    return "pv" if workload.startswith("pv") else "q8" if workload.endswith("_q8") else "linear"
 
 
 def gemm_source_hash(family="linear"):
@@ -293,8 +342,7 @@ def measured_traffic(workload, r):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.strip()
-    family = "pv" if workload.startswith("pv") else "linear"
-    if rec.get("source_sha256") != gemm_source_hash(family):
+    if rec.get("source_sha256") != gemm_source_hash(source_family(workload)):
         return None
     try:
         return float(rec["traffic_bytes_per_launch"])
@@ -393,24 +441,24 @@ def main():
     per_r = {}
     for r in ratios:
         stages, kk = W.stages(r)
-        ms_step, per = time_stages(torch, stages, args.steps, args.warmup)
-        gemm_name = stages[-1][0]
+        ms_step, per, gemm_ms = time_stages(torch, stages, args.steps, args.warmup)
         fl = W.flops(r)
-        per_r[r] = dict(kk=kk, ms_per_step=ms_step, stage_ms=per, step_tflops=fl / (ms_step * 1e-3) / 1e12,
-                        gemm_tflops=fl / (per[gemm_name] * 1e-3) / 1e12,
-                        gemm_gbs=W.gemm_bytes(r) / (per[gemm_name] * 1e-3) / 1e9)
+        per_r[r] = dict(kk=kk, ms_per_step=ms_step, stage_ms=per, gemm_ms=gemm_ms,
+                        step_tflops=fl / (ms_step * 1e-3) / 1e12,
+                        gemm_tflops=fl / (gemm_ms * 1e-3) / 1e12,
+                        gemm_gbs=W.gemm_bytes(r) / (gemm_ms * 1e-3) / 1e9)
         log(f"[bench] r={r}: kk={kk} step {ms_step * 1e3:.1f} us, stages "
             + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in per.items())
-            + f", gemm {per_r[r]['gemm_tflops']:.1f} TFLOP/s {per_r[r]['gemm_gbs']:.0f} GB/s")
+            + f"; gemm back to back {gemm_ms * 1e3:.1f} us, {per_r[r]['gemm_tflops']:.1f} TFLOP/s "
+            f"{per_r[r]['gemm_gbs']:.0f} GB/s")
         del stages
     base = per_r[1.0]
-    gname = "gemm"
     for r, v in per_r.items():
         v["speedup_step_vs_r1"] = base["ms_per_step"] / v["ms_per_step"]
-        v["speedup_gemm_vs_r1"] = base["stage_ms"][gname] / v["stage_ms"][gname]
+        v["speedup_gemm_vs_r1"] = base["gemm_ms"] / v["gemm_ms"]
 
     h = per_r[headline]
-    gemm_ms = h["stage_ms"][gname]
+    gemm_ms = h["gemm_ms"]
     if W.bound == "mfma":
         achieved = W.flops(headline) / (gemm_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
@@ -428,7 +476,8 @@ def main():
     if not args.no_cpu_baseline:
         groups = args.cpu_groups
         if groups is None:
-            groups = {"attn_proj": 24, "mlp_down": 1, "decode": 1, "tiny": 1, "pv4k": 8, "pv16k": 2}[W.name]
+            groups = {"attn_proj": 24, "mlp_down": 1, "decode": 1, "decode_q8": 1, "tiny": 1, "pv4k": 8,
+                      "pv16k": 2}[W.name]
         log(f"[bench] oracle baseline on {groups} groups ...")
         cpu = W.cpu_baseline(headline, groups)
         log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s ({cpu['seconds']} s)")
@@ -446,7 +495,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded stand-in for the pages' model activations and weights)",
-        "config": {"workload": W.describe(headline), "r": headline, "parallelism": "single GPU"},
+        "config": {"workload": W.describe(headline), "r": headline, "parallelism": "single GPU",
+                   **({"weights": "int8"} if getattr(W, "q8", False) else {})},
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_r": {str(r): {k: (round(x, 5) if isinstance(x, float) else

@@ -6,7 +6,10 @@
 #include "../../include/rmm.h"
 #include "rmm_internal.h"
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
+#include <unistd.h>
 
 using namespace rmm;
 
@@ -33,6 +36,17 @@ bool ok_matrix(const void *p, int dt, int64_t cols, int64_t ld)
 hipStream_t as_stream(void *s) { return (hipStream_t)s; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RMM_OK : RMM_EHIP; }
+
+// A distinct 62-bit tag per int8 GEMM call in this process, starting from a
+// per-process seed, so that tags left in a workspace by any earlier call (or
+// process) do not match the current call's.
+unsigned long long next_epoch()
+{
+    static std::atomic<unsigned long long> counter{
+        ((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
+         ((unsigned long long)getpid() << 40)) * 0x9E3779B97F4A7C15ull};
+    return counter.fetch_add(1) & ((1ull << 62) - 1);
+}
 
 }  // namespace
 
@@ -170,9 +184,16 @@ int rmm_rownorms_q8(const int8_t *Bq, int64_t ldq, const float *scale, int64_t K
     return hip_status(launch_rownorms_q8(Bq, ldq, scale, K, N, bnorm, as_stream(stream)));
 }
 
+size_t rmm_gemm_q8_workspace_bytes(int64_t M, int64_t N, int64_t kk, int64_t group_rows)
+{
+    (void)kk;
+    if (M < 1 || N < 1 || group_rows < 1) return 0;
+    return gemm_q8_workspace_bytes(M, N, group_rows);
+}
+
 int rmm_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq, const float *scale,
                 const int32_t *idx, int64_t ldidx, int64_t M, int64_t N, int64_t kk, int64_t group_rows,
-                void *Y, int ydt, int64_t ldy, void *stream)
+                void *Y, int ydt, int64_t ldy, void *ws, size_t ws_bytes, void *stream)
 {
     if (M < 1 || N < 1 || kk < 1 || group_rows < 1) return RMM_EINVAL;
     if (!ok_matrix(A, RMM_BF16, kk, lda)) return RMM_EINVAL;
@@ -183,8 +204,10 @@ int rmm_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq, c
     if (kk > INT32_MAX || (M + group_rows - 1) / group_rows > INT32_MAX / 64 ||
         (double)((M + group_rows - 1) / group_rows) * ((group_rows + 63) / 64) * ((N + 127) / 128) > INT32_MAX / 2)
         return RMM_EUNSUPPORTED;
+    const size_t need = gemm_q8_workspace_bytes(M, N, group_rows);
+    if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
     return hip_status(launch_gemm_q8(A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy,
-                                     as_stream(stream)));
+                                     ws, next_epoch(), as_stream(stream)));
 }
 
 size_t rmm_attn_pv_workspace_bytes(int64_t H, int64_t L, int64_t D, double r, int64_t qblock,

@@ -20,7 +20,8 @@
 //
 // Pipeline (D slabs ahead, NSTAGE = D + 1 ring stages, index ring 2D):
 //   prologue  IDX(0..D-1), wait; then IDX(p+D), AB(p) for p = 0..D-1
-//   step i    wait for AB(i); barrier; IDX(i+2D), AB(i+D); MFMAs on slab i
+//   step i    wait for AB(i); barrier; LDS reads (rows of slab i+D, all
+//             fragments of slab i); IDX(i+2D), AB(i+D); MFMAs on slab i
 // AB(x) needs the index slab x, issued before AB(x-D); waiting for AB(x-D)
 // therefore also covers it.  Every step issues the same operations (slabs
 // past the end reload valid memory: the last A slab and row 0 of B), so the
@@ -103,18 +104,20 @@ k_gemm_sk(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
             dma4(I + j, iring0 + (kt % S::IDX_RING) * BK * 4);
         }
     };
-    // this wave's share of slab kt (past the end: the last A slab, B row 0)
-    // into ring stage kt % NSTAGE; B row indices read before any DMA
-    auto issue_ab = [&](int kt) {
-        const int64_t kbase = (int64_t)kt * BK;
-        const int64_t abase = (int64_t)(kt < nkt ? kt : nkt - 1) * BK;
-        int32_t kr[S::B_SHARE];
+    // B row indices of slab kt (this wave's DMA lanes), from the index ring
+    auto load_rows = [&](int kt, int32_t (&kr)[S::B_SHARE]) {
 #pragma unroll
         for (int i = 0; i < S::B_SHARE; ++i) {
             const int jr = (wave * S::B_SHARE + i) * 4 + (lane >> 4);
             if constexpr (IDX) kr[i] = iring[wave][kt % S::IDX_RING][jr];
-            else kr[i] = (int32_t)(kbase + jr);
+            else kr[i] = kt * BK + jr;
         }
+    };
+    // this wave's share of slab kt (past the end: the last A slab, B row 0)
+    // into ring stage kt % NSTAGE
+    auto issue_ab = [&](int kt, const int32_t (&kr)[S::B_SHARE]) {
+        const int64_t kbase = (int64_t)kt * BK;
+        const int64_t abase = (int64_t)(kt < nkt ? kt : nkt - 1) * BK;
         const uint16_t *brow[S::B_SHARE];
 #pragma unroll
         for (int i = 0; i < S::B_SHARE; ++i) {
@@ -153,43 +156,59 @@ k_gemm_sk(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
 #pragma unroll
     for (int p = 0; p < D; ++p) {
         issue_idx(p + D);
-        issue_ab(p);
+        int32_t kr[S::B_SHARE];
+        load_rows(p, kr);
+        issue_ab(p, kr);
     }
 
+    // Each step reads the row indices of slab kt+D and every fragment of slab
+    // kt from LDS in one batch, issues the DMA of slab kt+D while those reads
+    // are in flight, and only then runs the MFMAs: one LDS round trip per slab
+    // instead of one per 16-deep k-step.
     for (int kt = 0; kt < nkt; ++kt) {
         vmwait<STEADY>();   // this wave's share of slab kt landed
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         // every wave's share of slab kt landed; stage (kt+D) % NSTAGE (slab
         // kt-1) has no reader left
-        issue_idx(kt + 2 * D);
-        issue_ab(kt + D);
+        int32_t kr[S::B_SHARE];
+        load_rows(kt + D, kr);
         const uint16_t *sa = smem + (kt % S::NSTAGE) * S::STAGE_ELEMS;
         const char *sb = (const char *)(sa + S::A_ELEMS);
-        const bool tail = (int64_t)(kt + 1) * BK > kk;
+        u32x4 af[KS][FM];
+        shortx4 blo[KS], bhi[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int c = 2 * ks + (lane >> 5);
-            bf16x8 af[FM];
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
                 const int r = fm * 32 + (lane & 31);
-                af[fm] = *(const bf16x8 *)(sa + r * BK + ((c ^ swz(r)) << 3));
-            }
-            if (tail) {
-                const int64_t k0 = (int64_t)kt * BK + ks * 16 + 8 * (lane >> 5);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (k0 + e >= kk)
-#pragma unroll
-                        for (int fm = 0; fm < FM; ++fm) af[fm][e] = (__bf16)0.0f;
+                af[ks][fm] = *(const u32x4 *)(sa + r * BK + ((c ^ swz(r)) << 3));
             }
             const char *p = sb + b_off + ks * 16 * TN * 2;
-            shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p));
-            shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p + 4 * TN * 2));
-            const bf16x8 bfr = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            blo[ks] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p));
+            bhi[ks] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p + 4 * TN * 2));
+        }
+        issue_idx(kt + 2 * D);
+        issue_ab(kt + D, kr);
+        if ((int64_t)(kt + 1) * BK > kk) {   // last slab: clear A columns at or past kk
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int64_t k0 = (int64_t)kt * BK + ks * 16 + 8 * (lane >> 5);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t m = (k0 + 2 * j < kk ? 0x0000ffffu : 0u) | (k0 + 2 * j + 1 < kk ? 0xffff0000u : 0u);
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) af[ks][fm][j] &= m;
+                }
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 bfr = __builtin_bit_cast(bf16x8, __builtin_shufflevector(blo[ks], bhi[ks], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
-                acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr, acc[fm], 0, 0, 0);
+                acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[ks][fm]), bfr,
+                                                                  acc[fm], 0, 0, 0);
         }
     }
     vmwait<0>();   // the trailing reloads: no DMA may land after the workgroup ends

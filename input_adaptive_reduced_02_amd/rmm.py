@@ -79,8 +79,10 @@ def _declare(L):
     L.rmm_quantize_q8.argtypes = [_P, _L, _L, _L, _P, _L, _P, _P]
     L.rmm_rownorms_q8.restype = _I
     L.rmm_rownorms_q8.argtypes = [_P, _L, _P, _L, _L, _P, _P]
+    L.rmm_gemm_q8_workspace_bytes.restype = _S
+    L.rmm_gemm_q8_workspace_bytes.argtypes = [_L, _L, _L, _L]
     L.rmm_gemm_q8.restype = _I
-    L.rmm_gemm_q8.argtypes = [_P, _L, _P, _L, _P, _P, _L, _L, _L, _L, _L, _P, _I, _L, _P]
+    L.rmm_gemm_q8.argtypes = [_P, _L, _P, _L, _P, _P, _L, _L, _L, _L, _L, _P, _I, _L, _P, _S, _P]
     return L
 
 
@@ -275,15 +277,21 @@ def rmm_rownorms_q8(Bq, scale, bnorm=None):
     return bnorm
 
 
-def rmm_gemm_q8(A, Bq, scale, idx, kk, group_rows, Y=None, ydt=torch.bfloat16, M=None):
+def rmm_gemm_q8_workspace_bytes(M, N, kk, group_rows):
+    return int(lib().rmm_gemm_q8_workspace_bytes(M, N, kk, group_rows))
+
+
+def rmm_gemm_q8(A, Bq, scale, idx, kk, group_rows, Y=None, ydt=torch.bfloat16, M=None, ws=None):
     """Y = scale * (A[:, :kk] * Bq[rows, :]) per group, rows as rmm_gemm."""
     M = A.shape[0] if M is None else M
     N = Bq.shape[1]
     if Y is None:
         Y = torch.empty((M, N), dtype=ydt, device=A.device)
+    need = rmm_gemm_q8_workspace_bytes(M, N, kk, group_rows)
+    w = _ws(need, A.device, ws)
     _check("rmm_gemm_q8", lib().rmm_gemm_q8(
         _ptr(A), _ld(A), _ptr(Bq), _ld(Bq), _ptr(scale), _ptr(idx), _ld(idx) if idx is not None else 0, M, N,
-        kk, group_rows, _ptr(Y), _dt(Y), _ld(Y), _stream(A)))
+        kk, group_rows, _ptr(Y), _dt(Y), _ld(Y), _ptr(w), need, _stream(A)))
     return Y
 
 

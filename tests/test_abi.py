@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -175,10 +175,15 @@ def test_validation_rejects_bad_arguments():
     assert L.rmm_rownorms_q8(P, 32, P2, 4, 24, P3, None) == EINVAL          # N % 16
     assert L.rmm_rownorms_q8(P, 32, None, 4, 32, P3, None) == EINVAL
     assert L.rmm_rownorms_q8(P, 32, P2, 4, 32, ctypes.c_void_p((3 << 20) + 4), None) == EINVAL
-    # gemm_q8(A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk, gr, Y, ydt, ldy, stream)
-    assert L.rmm_gemm_q8(P, 64, P2, 32, P3, None, 0, 64, 24, 64, 64, P3, BF, 24, None) == EINVAL   # N % 16
-    assert L.rmm_gemm_q8(P, 64, P2, 32, None, None, 0, 64, 32, 64, 64, P3, BF, 32, None) == EINVAL  # no scale
-    assert L.rmm_gemm_q8(P, 32, P2, 32, P3, None, 0, 64, 32, 64, 64, P3, BF, 32, None) == EINVAL    # lda < kk
-    assert L.rmm_gemm_q8(P, 64, P2, 32, P3, P, 32, 64, 32, 64, 64, P3, BF, 32, None) == EINVAL      # ldidx < kk
-    assert L.rmm_gemm_q8(P, 64, P2, 40, P3, None, 0, 64, 32, 64, 64, P3, BF, 32, None) == EINVAL    # ldq % 16
-    assert L.rmm_gemm_q8(P, 64, P2, 32, P3, None, 0, 64, 32, 64, 64, P3, 5, 32, None) == EINVAL     # ydt
+    # gemm_q8(A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk, gr, Y, ydt, ldy, ws, wsb, stream)
+    W = 1 << 30
+    assert L.rmm_gemm_q8(P, 64, P2, 32, P3, None, 0, 64, 24, 64, 64, P3, BF, 24, P3, W, None) == EINVAL   # N % 16
+    assert L.rmm_gemm_q8(P, 64, P2, 32, None, None, 0, 64, 32, 64, 64, P3, BF, 32, P3, W, None) == EINVAL  # no scale
+    assert L.rmm_gemm_q8(P, 32, P2, 32, P3, None, 0, 64, 32, 64, 64, P3, BF, 32, P3, W, None) == EINVAL    # lda < kk
+    assert L.rmm_gemm_q8(P, 64, P2, 32, P3, P, 32, 64, 32, 64, 64, P3, BF, 32, P3, W, None) == EINVAL      # ldidx < kk
+    assert L.rmm_gemm_q8(P, 64, P2, 40, P3, None, 0, 64, 32, 64, 64, P3, BF, 32, P3, W, None) == EINVAL    # ldq % 16
+    assert L.rmm_gemm_q8(P, 64, P2, 32, P3, None, 0, 64, 32, 64, 64, P3, 5, 32, P3, W, None) == EINVAL     # ydt
+    need = L.rmm_gemm_q8_workspace_bytes(64, 28672, 4096, 64)
+    assert need == 112 * 2 * 64 * 256 * 4 + 112 * 8
+    assert L.rmm_gemm_q8_workspace_bytes(2048, 4096, 4096, 128) == 0            # 512 tiles: no split
+    assert L.rmm_gemm_q8(P, 64, P2, 32, P3, None, 0, 64, 32, 64, 64, P3, BF, 32, P3, 16, None) == EINVAL   # short ws
