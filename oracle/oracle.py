@@ -297,7 +297,7 @@ def pv_select_block(Pt, V, L, qblock, g, r, causal=True, lib=None):
 # ---------------------------------------------------------------- int8 weights
 def quantize_q8(B, lib=None):
     """(q int8 [K, N], scale float32 [N]) of a weight given as binary32 values
-    (bf16 weights widened exactly), reading R7."""
+    (bf16 weights widened exactly), reading R9."""
     lib = lib or load()
     B = np.ascontiguousarray(B, dtype=np.float32)
     K, N = B.shape

@@ -41,7 +41,7 @@
  *      k < K_g = min(L, qblock*(g+1)); the score of key k is
  *      (sum over the block's queries of P[q,k]) * ||V[k,:]||_2; k_g = kk(r, K_g).
  *   R6 every sum runs in ascending index order.
- *   R7 int8 weights ("Resultados Experimentais", item "Compatibilidade":
+ *   R9 int8 weights ("Resultados Experimentais", item "Compatibilidade":
  *      the method works on INT8-quantised weights; the pages fix no scheme).
  *      Symmetric absmax quantisation with one binary32 scale per output
  *      column n: s_n = max_k |B[k,n]| / 127, q[k,n] = round-half-even(B[k,n]
@@ -293,7 +293,7 @@ double oracle_pv_bound(const double *Ptb, int64_t ldp, int64_t nq, const double 
     return beta;
 }
 
-/* ---- int8 weight quantisation, reading R7.  B is K x N binary32 (row stride
+/* ---- int8 weight quantisation, reading R9.  B is K x N binary32 (row stride
  * ldb); writes q (row stride ldq) and one scale per column. */
 void oracle_quantize_q8(const float *B, int64_t K, int64_t N, int64_t ldb, int8_t *q, int64_t ldq,
                         float *scale)
@@ -322,7 +322,7 @@ void oracle_quantize_q8(const float *B, int64_t K, int64_t N, int64_t ldb, int8_
     }
 }
 
-/* ---- the dequantised weight of reading R7: Bd[k][n] = s_n * q[k][n], exact
+/* ---- the dequantised weight of reading R9: Bd[k][n] = s_n * q[k][n], exact
  * in binary64 (a 24-bit by 8-bit product). */
 void oracle_dequant_q8(const int8_t *q, int64_t ldq, const float *scale, int64_t K, int64_t N,
                        double *Bd, int64_t ldd)
@@ -332,7 +332,7 @@ void oracle_dequant_q8(const int8_t *q, int64_t ldq, const float *scale, int64_t
             Bd[k * ldd + n] = (double)scale[n] * (double)q[k * ldq + n];
 }
 
-/* ---- row norms of the dequantised weight (reading R7 with R1):
+/* ---- row norms of the dequantised weight (reading R9 with R1):
  * b[k] = ||(s_n q[k][n])_n||_2, ascending n. */
 void oracle_rownorms_q8(const int8_t *q, int64_t ldq, const float *scale, int64_t K, int64_t N,
                         double *b)
