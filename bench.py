@@ -94,6 +94,7 @@ class Linear:
         # at least 280 MB of other weight rows stream by, and every step reads
         # its weight from HBM, as a real decode step would.
         copies = {"decode": 3, "decode_q8": 8}.get(name, 1)
+        self.copies = copies
         self.Bs = [self.B] + [self.B.clone() for _ in range(copies - 1)]
         self._rot = 0
         torch.cuda.synchronize()
@@ -119,7 +120,7 @@ class Linear:
         self.kk = kk
         Y = torch.empty((self.M, self.N), dtype=torch.float32 if self.f32 else torch.bfloat16, device=self.dev)
         if self.q8:
-            wq = torch.empty(max(1, rmm.rmm_gemm_q8_workspace_bytes(self.M, self.N, kk, self.gr)),
+            wq = torch.zeros(max(1, rmm.rmm_gemm_q8_workspace_bytes(self.M, self.N, kk, self.gr)),
                              dtype=torch.uint8, device=self.dev)
         if self.q8 and kk == self.K:
             return [("gemm", lambda: rmm.rmm_gemm_q8(self.A, self.next_B(), self.scale, None, kk, self.gr,
@@ -200,6 +201,7 @@ class PV:
         from input_adaptive_reduced_02_amd import rmm, synth
         self.rmm, self.torch = rmm, torch
         self.H, self.L, self.D = 32, L, 128
+        self.copies = 1
         self.name = f"pv{L // 1024}k"
         self.ratios = synth.RATIOS["pv"]
         self.dev = dev

@@ -230,7 +230,8 @@ int rmm_rownorms_q8(const int8_t *Bq, int64_t ldq, const float *scale, int64_t K
 
 /* Workspace bytes rmm_gemm_q8 needs: 0, or, when the output has at most 128
  * tiles of 64 x 256 (each then split over two workgroups along the kept
- * rows), two fp32 64 x 256 partial tiles and one 8-byte tag per tile. */
+ * rows), two fp32 64 x 256 partial tiles and one 4-byte arrival counter per
+ * tile. */
 size_t rmm_gemm_q8_workspace_bytes(int64_t M, int64_t N, int64_t kk, int64_t group_rows);
 
 /* The reduced product on an int8 weight:
@@ -239,9 +240,11 @@ size_t rmm_gemm_q8_workspace_bytes(int64_t M, int64_t N, int64_t kk, int64_t gro
  * kk == K).  A is the bf16 panel of rmm_gemm.  Each product of a bf16 value
  * and a code is exact in fp32; the sum is accumulated in fp32 in a fixed
  * order (deterministic), and the scale multiplies it once; Y as rmm_gemm.
- * ws: rmm_gemm_q8_workspace_bytes(...) bytes, 16-byte aligned, any content
- * (it holds partial sums and per-call tags; calls that share a workspace must
- * not overlap).  Errors: RMM_EINVAL for bad pointers/sizes/workspace. */
+ * ws: rmm_gemm_q8_workspace_bytes(...) bytes, 16-byte aligned, ZERO-FILLED
+ * before its first use with this shape; each call leaves it ready for the
+ * next (its counters stay even), so a zero-filled workspace can be reused,
+ * also by launches replayed from a HIP graph.  Calls that share a workspace
+ * must not overlap.  Errors: RMM_EINVAL for bad pointers/sizes/workspace. */
 int rmm_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq, const float *scale,
                 const int32_t *idx, int64_t ldidx, int64_t M, int64_t N, int64_t kk, int64_t group_rows,
                 void *Y, int ydt, int64_t ldy, void *ws, size_t ws_bytes, void *stream);

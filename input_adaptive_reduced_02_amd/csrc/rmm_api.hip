@@ -6,10 +6,7 @@
 #include "../../include/rmm.h"
 #include "rmm_internal.h"
 
-#include <atomic>
-#include <chrono>
 #include <cmath>
-#include <unistd.h>
 
 using namespace rmm;
 
@@ -36,17 +33,6 @@ bool ok_matrix(const void *p, int dt, int64_t cols, int64_t ld)
 hipStream_t as_stream(void *s) { return (hipStream_t)s; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RMM_OK : RMM_EHIP; }
-
-// A distinct 62-bit tag per int8 GEMM call in this process, starting from a
-// per-process seed, so that tags left in a workspace by any earlier call (or
-// process) do not match the current call's.
-unsigned long long next_epoch()
-{
-    static std::atomic<unsigned long long> counter{
-        ((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
-         ((unsigned long long)getpid() << 40)) * 0x9E3779B97F4A7C15ull};
-    return counter.fetch_add(1) & ((1ull << 62) - 1);
-}
 
 }  // namespace
 
@@ -207,7 +193,7 @@ int rmm_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq, c
     const size_t need = gemm_q8_workspace_bytes(M, N, group_rows);
     if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
     return hip_status(launch_gemm_q8(A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy,
-                                     ws, next_epoch(), as_stream(stream)));
+                                     ws, as_stream(stream)));
 }
 
 size_t rmm_attn_pv_workspace_bytes(int64_t H, int64_t L, int64_t D, double r, int64_t qblock,

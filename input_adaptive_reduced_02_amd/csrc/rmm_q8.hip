@@ -217,7 +217,7 @@ k_gemm_q8(const uint16_t *__restrict__ A, int64_t lda, const int8_t *__restrict_
           const float *__restrict__ scale, const int32_t *__restrict__ idx, int64_t ldidx, int64_t M,
           int64_t N, int64_t kk, int64_t gr, void *__restrict__ Y, int ydt, int64_t ldy,
           int tiles_per_group, int m_tiles, int n_tiles, int ksplit, float *__restrict__ part_ws,
-          unsigned long long *__restrict__ tags, unsigned long long epoch)
+          unsigned int *__restrict__ arrivals)
 {
     using S = Q8Shape;
     constexpr int TM = S::TM, TN = S::TN, BK = S::BK, FM = S::FM, FN = S::FN, KS = S::KS;
@@ -431,14 +431,14 @@ k_gemm_q8(const uint16_t *__restrict__ A, int64_t lda, const int8_t *__restrict_
     // ---- split over workgroups: the two parts of a tile meet in global
     // memory (thread-major: element e of thread x at e * threads + x, so
     // every store and load of a wave is one 256-byte run).  Each part stores
-    // its sum with agent-coherent stores, waits for
-    // them to complete, then swaps its tag (epoch, part) into the tile's tag
-    // word; the part that finds the other part's tag of this epoch arrives
-    // second, reads the other sum with agent-coherent loads and adds the two
-    // in part order (the first part simply ends).  Only these words are made
-    // coherent -- no cache-wide write-back or invalidation.  Any earlier
-    // content of the tag word differs from this epoch's tags, so the
-    // workspace needs no clearing.
+    // its sum with agent-coherent stores, waits for them to complete, then
+    // adds 1 to the tile's arrival counter; the part that finds the counter
+    // odd arrives second, reads the other sum with agent-coherent loads and
+    // adds the two in part order (the first part simply ends).  Only these
+    // words are made coherent -- no cache-wide write-back or invalidation.
+    // Every call adds 2 to each counter, so counters that start even (a
+    // zero-filled workspace) stay even from call to call, also when the
+    // launch is replayed from a graph.
     if (ksplit == 2) {
         float *mine_ws = part_ws + ((int64_t)tile * 2 + kpart) * (TM * TN);
 #pragma unroll
@@ -451,10 +451,9 @@ k_gemm_q8(const uint16_t *__restrict__ A, int64_t lda, const int8_t *__restrict_
         __syncthreads();                                     // ... and of every wave
         __shared__ int second;
         if (threadIdx.x == 0) {
-            const unsigned long long mine_tag = (epoch << 1) | (unsigned long long)kpart;
-            const unsigned long long old =
-                __hip_atomic_exchange(tags + tile, mine_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            second = old == ((epoch << 1) | (unsigned long long)(1 - kpart));
+            const unsigned int old =
+                __hip_atomic_fetch_add(arrivals + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            second = (int)(old & 1u);
         }
         __syncthreads();
         if (!second) return;
@@ -540,7 +539,8 @@ hipError_t launch_rownorms_q8(const int8_t *q, int64_t ldq, const float *scale, 
 
 // Tiles of 64 x 256; when there are at most 128 tiles (fewer than half the
 // CUs) every tile is split into two halves of its kept rows, each on its own
-// workgroup, which meet through the workspace.
+// workgroup, which meet through the workspace (two fp32 partial tiles and a
+// 4-byte arrival counter per tile).
 int q8_ksplit(int64_t M, int64_t N, int64_t group_rows)
 {
     using S = Q8Shape;
@@ -555,13 +555,12 @@ size_t gemm_q8_workspace_bytes(int64_t M, int64_t N, int64_t group_rows)
     if (q8_ksplit(M, N, group_rows) == 1) return 0;
     const int64_t G = (M + group_rows - 1) / group_rows;
     const int64_t tiles = G * ((group_rows + S::TM - 1) / S::TM) * ((N + S::TN - 1) / S::TN);
-    return (size_t)tiles * 2 * S::TM * S::TN * sizeof(float) + (size_t)tiles * 8;
+    return (size_t)tiles * 2 * S::TM * S::TN * sizeof(float) + (size_t)tiles * 4;
 }
 
 hipError_t launch_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq,
                           const float *scale, const int32_t *idx, int64_t ldidx, int64_t M, int64_t N,
-                          int64_t kk, int64_t group_rows, void *Y, int ydt, int64_t ldy, void *ws,
-                          unsigned long long epoch, hipStream_t s)
+                          int64_t kk, int64_t group_rows, void *Y, int ydt, int64_t ldy, void *ws, hipStream_t s)
 {
     using S = Q8Shape;
     const int64_t G = (M + group_rows - 1) / group_rows;
@@ -571,15 +570,15 @@ hipError_t launch_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int6
     const int ksplit = q8_ksplit(M, N, group_rows);
     const int total = m_tiles * n_tiles * ksplit;
     float *part_ws = (float *)ws;
-    unsigned long long *tags =
-        ksplit == 2 ? (unsigned long long *)((char *)ws + (size_t)m_tiles * n_tiles * 2 * S::TM * S::TN * 4) : nullptr;
+    unsigned int *arrivals =
+        ksplit == 2 ? (unsigned int *)((char *)ws + (size_t)m_tiles * n_tiles * 2 * S::TM * S::TN * 4) : nullptr;
     const dim3 grid((unsigned)(8 * ((total + 7) / 8))), block(64 * S::NW);
     if (idx)
         hipLaunchKernelGGL(k_gemm_q8<true>, grid, block, 0, s, A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk,
-                           group_rows, Y, ydt, ldy, tiles_per_group, m_tiles, n_tiles, ksplit, part_ws, tags, epoch);
+                           group_rows, Y, ydt, ldy, tiles_per_group, m_tiles, n_tiles, ksplit, part_ws, arrivals);
     else
         hipLaunchKernelGGL(k_gemm_q8<false>, grid, block, 0, s, A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk,
-                           group_rows, Y, ydt, ldy, tiles_per_group, m_tiles, n_tiles, ksplit, part_ws, tags, epoch);
+                           group_rows, Y, ydt, ldy, tiles_per_group, m_tiles, n_tiles, ksplit, part_ws, arrivals);
     return hipGetLastError();
 }
 

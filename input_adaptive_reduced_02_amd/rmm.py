@@ -282,12 +282,15 @@ def rmm_gemm_q8_workspace_bytes(M, N, kk, group_rows):
 
 
 def rmm_gemm_q8(A, Bq, scale, idx, kk, group_rows, Y=None, ydt=torch.bfloat16, M=None, ws=None):
-    """Y = scale * (A[:, :kk] * Bq[rows, :]) per group, rows as rmm_gemm."""
+    """Y = scale * (A[:, :kk] * Bq[rows, :]) per group, rows as rmm_gemm.  A
+    caller's `ws` must be zero-filled before its first use (it stays reusable)."""
     M = A.shape[0] if M is None else M
     N = Bq.shape[1]
     if Y is None:
         Y = torch.empty((M, N), dtype=ydt, device=A.device)
     need = rmm_gemm_q8_workspace_bytes(M, N, kk, group_rows)
+    if ws is None and need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=A.device)   # zero-filled before first use
     w = _ws(need, A.device, ws)
     _check("rmm_gemm_q8", lib().rmm_gemm_q8(
         _ptr(A), _ld(A), _ptr(Bq), _ld(Bq), _ptr(scale), _ptr(idx), _ld(idx) if idx is not None else 0, M, N,

@@ -191,3 +191,56 @@ def test_full_decode_chain(decode_q8, r):
     idx, scores, Y = run_chain_q8(c["A"], c["Bq"], c["s"], c["bnorm"], r, 64)
     rows = np.array([0, 17, 40, M - 1])
     check_chain(c["A64"], O.dequant_q8(c["q"], c["sg"]), b_ref, idx, scores, Y, r, 64, tag, rows=rows)
+
+
+def test_workspace_reuse_and_graph_replay():
+    """One zero-filled workspace serves consecutive calls of different sizes,
+    and the chain captured in a HIP graph gives the eager result on every
+    replay (eager work and synchronisations between the replays)."""
+    M, K, N, gr = 64, 2048, 4096, 64
+    d = synth.linear_inputs("decode", M, K, N, seed=8)
+    A = up_bf16(d["A"])
+    Bq, s = rmm.rmm_quantize_q8(up_bf16(weight_bits(K, N, seed=3)))
+    bn = rmm.rmm_rownorms_q8(Bq, s)
+    need = max(rmm.rmm_gemm_q8_workspace_bytes(M, N, rmm.rmm_kk(r, K), gr) for r in (0.3, 0.5, 1.0))
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    ref = {}
+    for r in (0.5, 0.3, 1.0, 0.5):
+        kk = rmm.rmm_kk(r, K)
+        idx = rmm.rmm_select(A, r, gr, bnorm=bn) if r < 1 else None
+        Ap = rmm.rmm_gather(A, idx, kk, gr)[0] if r < 1 else A
+        Yw = rmm.rmm_gemm_q8(Ap, Bq, s, idx, kk, gr, ws=ws)
+        Yf = rmm.rmm_gemm_q8(Ap, Bq, s, idx, kk, gr)   # fresh zero-filled workspace
+        torch.cuda.synchronize()
+        assert np.array_equal(down(Yw), down(Yf)), f"reused workspace differs at r={r}"
+        ref[r] = down(Yf)
+    # graph: select -> gather -> GEMM at r = 0.5 on fixed buffers
+    r, kk = 0.5, rmm.rmm_kk(0.5, K)
+    idx = torch.zeros((1, rmm.rmm_kk_pad(kk)), dtype=torch.int32, device=DEV)
+    Ap = torch.empty((M, rmm.rmm_kk_pad(kk)), dtype=torch.bfloat16, device=DEV)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    sws = torch.empty(max(1, rmm.rmm_select_workspace_bytes(M, K, gr)), dtype=torch.uint8, device=DEV)
+
+    def step():
+        rmm.rmm_select(A, r, gr, bnorm=bn, idx=idx, ws=sws)
+        rmm.rmm_gather(A, idx, kk, gr, Apanel=Ap)
+        rmm.rmm_gemm_q8(Ap, Bq, s, idx, kk, gr, Y=Y, ws=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        Y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(down(Y), ref[0.5]), f"graph replay {rep} differs"
+        step()   # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(down(Y), ref[0.5])
