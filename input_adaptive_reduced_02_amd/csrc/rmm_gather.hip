@@ -9,9 +9,10 @@
 // HBM-bound data movement.  Picking 2-byte elements straight out of global
 // memory costs the load units a cache-line access per element, so whole rows
 // of A are first copied into LDS with coalesced 16-byte loads (a workgroup
-// holds up to 32 KiB of rows), then every thread picks 8 kept elements of a
-// row out of LDS by index and writes them as one 16-byte panel chunk.  The
-// global traffic is exactly one read of A and one write of the panel.
+// stages about 8 KiB of rows, a single row up to 32 KiB), then every thread
+// picks 8 kept elements of a row out of LDS by index and writes them as one
+// 16-byte panel chunk.  The global traffic is exactly one read of A and one
+// write of the panel.
 #include "rmm_internal.h"
 
 namespace rmm {
@@ -59,7 +60,7 @@ k_gather_a(const void *__restrict__ Av, int64_t M, int64_t lda, const int32_t *_
     *(uint4 *)(Ap + m * ldp + j0) = o;
 }
 
-constexpr int kGatherLds = 32768;   // bytes of A rows staged per workgroup
+constexpr int kGatherLds = 32768;   // longest A row (bytes) staged in LDS
 
 // One workgroup per `rpw` consecutive rows: the rows go to LDS (16-byte
 // chunks, the ragged end of a row element by element), then thread t writes
@@ -152,8 +153,11 @@ hipError_t launch_gather(const void *A, int dt, int64_t M, int64_t K, int64_t ld
     const int64_t cpr = kpad / 8;
     const int64_t row_bytes = (K * (dt == 1 ? 2 : 4) + 15) / 16 * 16;
     if (row_bytes <= kGatherLds) {
-        int rpw = (int)(kGatherLds / row_bytes);
+        // rows per workgroup: about 8 KiB of rows, so that many small
+        // workgroups overlap one another's load and write phases on a CU
+        int rpw = (int)(8192 / row_bytes);
         if (rpw > 8) rpw = 8;
+        if (rpw < 1) rpw = 1;
         const unsigned blocks = (unsigned)((M + rpw - 1) / rpw);
         const size_t lds = (size_t)rpw * row_bytes;
         if (dt == 1)

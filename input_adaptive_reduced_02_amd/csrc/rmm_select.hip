@@ -129,10 +129,23 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     if (tid == 0) s_last = 0;   // written again (by the kk-th keeper) after several barriers
     int32_t key[KPT];           // -1 marks "no key here"; real keys are >= 0
     int32_t lo = 0x7fffffff, hi = 0;
+    if (KPT % 4 == 0 && kpt == KPT && base + KPT <= K && ((uintptr_t)(s + base) & 15u) == 0) {
+        // a full, aligned run of keys: 16-byte loads
+#pragma unroll
+        for (int i = 0; i < KPT; i += 4) {
+            const u32x4 v = *(const u32x4 *)(s + base + i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) key[i + e] = (int32_t)v[e];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int64_t k = base + i;
+            key[i] = (i < kpt && k < K) ? __float_as_int(s[k]) : -1;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        const int64_t k = base + i;
-        key[i] = (i < kpt && k < K) ? __float_as_int(s[k]) : -1;
         if (key[i] >= 0) {
             lo = min(lo, key[i]);
             hi = max(hi, key[i]);
