@@ -8,8 +8,8 @@ nothing from the GPU package.
 Source of the method: "Reduced Matrix Multiplication: Input-Adaptive
 Matrix-Product Reduction for LLM Inference", technical summary (gist.science),
 section "Metodologia" (Mecanismo Central; Estratégia de Seleção; Escopo de
-Aplicação).  The readings R1-R6 taken where the pages are silent are listed in
-the header of rmm_oracle.c.
+Aplicação).  The readings taken where the pages are silent (R1-R6, R9-R11) are
+listed in the header of rmm_oracle.c.
 """
 import ctypes
 import os
@@ -79,6 +79,10 @@ def _declare(lib):
     lib.oracle_dequant_q8.argtypes = [_I8, _L, _F, _L, _L, _D, _L]
     lib.oracle_rownorms_q8.restype = None
     lib.oracle_rownorms_q8.argtypes = [_I8, _L, _F, _L, _L, _D]
+    lib.oracle_qk_scores.restype = None
+    lib.oracle_qk_scores.argtypes = [_D, _D, _L, _L, _L, _L, ctypes.c_int, _D, _F]
+    lib.oracle_attn_probs.restype = None
+    lib.oracle_attn_probs.argtypes = [_D, _D, _L, _L, _L, _L, ctypes.c_int, _I32, _L, _D]
 
 
 def _p(a, typ):
@@ -294,6 +298,50 @@ def pv_select_block(Pt, V, L, qblock, g, r, causal=True, lib=None):
                 near=near_ties(s64, s32, idx))
 
 
+# ---------------------------------------------------------------- QK^T and the probabilities
+def qk_scores(Q, K, q0, nq, Kg, use_k=True, lib=None):
+    """(s64, s32) of the D features for queries q0 .. q0+nq-1 of one head
+    (Q, K: [L, D]) with candidate keys k < Kg, reading R10."""
+    lib = lib or load()
+    Q = _f64(Q)
+    K = _f64(K)
+    D = Q.shape[1]
+    s64 = np.empty(D, np.float64)
+    s32 = np.empty(D, np.float32)
+    lib.oracle_qk_scores(_p(Q, _D), _p(K, _D), D, q0, nq, Kg, int(bool(use_k)), _p(s64, _D), _p(s32, _F))
+    return s64, s32
+
+
+def qk_select_block(Q, K, qblock, g, r, causal=True, use_k=True, lib=None):
+    """Kept features of one (head, query block): dict(Kg, kk, idx, s64, s32, near)."""
+    lib = lib or load()
+    L, D = Q.shape
+    q0 = g * qblock
+    nq = min(qblock, L - q0)
+    Kg = pv_prefix(L, qblock, g, causal, lib)
+    s64, s32 = qk_scores(Q, K, q0, nq, Kg, use_k, lib)
+    kk_ = kk(r, D, lib)
+    idx = topk(s32, kk_, lib)
+    return dict(Kg=Kg, kk=kk_, idx=idx, s64=s64, s32=s32, near=near_ties(s64, s32, idx))
+
+
+def attn_probs(Q, K, q0, nq, causal=True, idx=None, lib=None):
+    """P [nq, L] float64: rows q0 .. q0+nq-1 of one head's attention
+    probabilities over the kept features idx (None: all), reading R11."""
+    lib = lib or load()
+    Q = _f64(Q)
+    K = _f64(K)
+    L, D = Q.shape
+    P = np.empty((nq, L), np.float64)
+    if idx is None:
+        lib.oracle_attn_probs(_p(Q, _D), _p(K, _D), L, D, q0, nq, int(bool(causal)), None, D, _p(P, _D))
+    else:
+        i = np.ascontiguousarray(idx, dtype=np.int32)
+        lib.oracle_attn_probs(_p(Q, _D), _p(K, _D), L, D, q0, nq, int(bool(causal)), _p(i, _I32), len(i),
+                              _p(P, _D))
+    return P
+
+
 # ---------------------------------------------------------------- int8 weights
 def quantize_q8(B, lib=None):
     """(q int8 [K, N], scale float32 [N]) of a weight given as binary32 values
@@ -333,5 +381,5 @@ __all__ = [
     "load", "widen_bf16", "widen_f32", "kk", "rownorms", "colnorms", "scores", "topk", "select",
     "reduced", "reduced_entries", "dense", "bound", "pv_prefix", "pv_block_inputs", "pv_scores",
     "pv_block", "pv_bound", "pv_select_block", "near_ties", "NEAR_TIE_REL",
-    "quantize_q8", "dequant_q8", "rownorms_q8",
+    "quantize_q8", "dequant_q8", "rownorms_q8", "qk_scores", "qk_select_block", "attn_probs",
 ]

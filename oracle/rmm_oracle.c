@@ -41,6 +41,19 @@
  *      k < K_g = min(L, qblock*(g+1)); the score of key k is
  *      (sum over the block's queries of P[q,k]) * ||V[k,:]||_2; k_g = kk(r, K_g).
  *   R6 every sum runs in ascending index order.
+ *   R10 QK^T ("Escopo de Aplicacao": the feature dimension of QK^T).  Here A
+ *      is a block of queries Q_g and B is K^T restricted to the keys the block
+ *      is multiplied with (its causal prefix k < K_g, as in R5; all L keys
+ *      without the mask), so the contraction runs over the head dimension D.
+ *      Feature j of block g scores ||Q[rows_g, j]||_2 * ||K[0 .. K_g-1, j]||_2
+ *      (the second factor dropped: the pages' activation-only rule) and
+ *      kk(r, D) features are kept per (head, block) with the R4 order.
+ *   R11 the logit of query q and candidate key k is the reduced dot product
+ *      over the kept features divided by sqrt(D), D the full head dimension
+ *      (the reduced product stands in for the full one, so the softmax keeps
+ *      the model's temperature).  P[q, .] is the softmax of row q over its
+ *      candidates (k <= q causal, else every k < L) and 0 elsewhere.  The
+ *      P.V scores of R5 are taken on P as stored for the product (bf16).
  *   R9 int8 weights ("Resultados Experimentais", item "Compatibilidade":
  *      the method works on INT8-quantised weights; the pages fix no scheme).
  *      Symmetric absmax quantisation with one binary32 scale per output
@@ -291,6 +304,73 @@ double oracle_pv_bound(const double *Ptb, int64_t ldp, int64_t nq, const double 
     }
     free(kept);
     return beta;
+}
+
+/* ---- QK^T feature scores of one query block, reading R10.  One head: Q and
+ * K are L x D row-major.  The block holds queries q0 .. q0+nq-1, its candidate
+ * keys are k < Kg.  s64[j] = ||Q[q0.., j]||_2 * ||K[0..Kg-1, j]||_2 (use_k == 0:
+ * ||Q[q0.., j]||_2 alone); s32 = s64 rounded once to binary32. */
+void oracle_qk_scores(const double *Q, const double *K, int64_t D, int64_t q0, int64_t nq, int64_t Kg,
+                      int use_k, double *s64, float *s32)
+{
+    for (int64_t j = 0; j < D; ++j) {
+        double qq = 0.0;
+        for (int64_t i = 0; i < nq; ++i) {
+            double v = Q[(q0 + i) * D + j];
+            qq += v * v;
+        }
+        double kn = 1.0;
+        if (use_k) {
+            double kq = 0.0;
+            for (int64_t k = 0; k < Kg; ++k) {
+                double v = K[k * D + j];
+                kq += v * v;
+            }
+            kn = sqrt(kq);
+        }
+        double s = sqrt(qq) * kn;
+        s64[j] = s;
+        s32[j] = (float)s;
+    }
+}
+
+/* ---- attention probabilities of queries q0 .. q0+nq-1 of one head, reading
+ * R11.  Kept features idx[0 .. kk-1] (idx == NULL: every feature, kk = D).
+ * Writes P[i*L + k] for the row of query q0+i: the softmax over the row's
+ * candidate keys of S[k] = (sum over kept j, ascending, of Q[q, j] K[k, j]) /
+ * sqrt(D), computed as exp(S[k] - max S) / sum of those terms; 0 for the keys
+ * the row does not see. */
+void oracle_attn_probs(const double *Q, const double *K, int64_t L, int64_t D, int64_t q0, int64_t nq,
+                       int causal, const int32_t *idx, int64_t kk, double *P)
+{
+    double *S = (double *)malloc((size_t)L * sizeof(double));
+    const int64_t nf = idx ? kk : D;
+    for (int64_t i = 0; i < nq; ++i) {
+        const int64_t q = q0 + i;
+        const int64_t n = causal ? q + 1 : L;
+        double *p = P + i * L;
+        double mx = -INFINITY;
+        for (int64_t k = 0; k < n; ++k) {
+            double dot = 0.0;
+            for (int64_t j = 0; j < nf; ++j) {
+                int64_t f = idx ? idx[j] : j;
+                dot += Q[q * D + f] * K[k * D + f];
+            }
+            S[k] = dot / sqrt((double)D);
+            if (S[k] > mx)
+                mx = S[k];
+        }
+        double sum = 0.0;
+        for (int64_t k = 0; k < n; ++k) {
+            p[k] = exp(S[k] - mx);
+            sum += p[k];
+        }
+        for (int64_t k = 0; k < n; ++k)
+            p[k] /= sum;
+        for (int64_t k = n; k < L; ++k)
+            p[k] = 0.0;
+    }
+    free(S);
 }
 
 /* ---- int8 weight quantisation, reading R9.  B is K x N binary32 (row stride

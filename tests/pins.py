@@ -455,9 +455,130 @@ def pin_q8_dequant_norms(lib):
     assert np.allclose(b, np.linalg.norm(want, axis=1), rtol=1e-13, atol=0)
 
 
+# ------------------------------------------------------------------ QK^T and probabilities
+def pin_qk_hand(lib):
+    """The hand-worked feature selection and probabilities of
+    tests/golden/hand_qk.txt (causal, every key, activation-only)."""
+    g = read_golden("hand_qk.txt")
+    Q = np.array(g["Q"], float)
+    K = np.array(g["K"], float)
+    qb = g["qblock"]
+    rows = []
+    for blk in g["blocks"]:
+        sel = O.qk_select_block(Q, K, qb, blk["g"], g["r"], True, True, lib)
+        assert sel["Kg"] == blk["Kg"] and sel["kk"] == 2
+        assert np.allclose(sel["s64"] ** 2, blk["scores_squared"], rtol=1e-15, atol=0)
+        assert list(sel["idx"]) == blk["I"]
+        nc = O.qk_select_block(Q, K, qb, blk["g"], g["r"], False, True, lib)
+        assert np.allclose(nc["s64"] ** 2, blk["noncausal_scores_squared"], rtol=1e-15, atol=0)
+        assert list(nc["idx"]) == blk["noncausal_I"]
+        ao = O.qk_select_block(Q, K, qb, blk["g"], g["r"], True, False, lib)
+        assert list(ao["idx"]) == blk["aonly_I"]
+        q0 = blk["g"] * qb
+        rows.append(O.attn_probs(Q, K, q0, qb, True, sel["idx"], lib))
+    P = np.vstack(rows)
+    want = np.array([[float(Fraction(str(x))) for x in row] for row in g["P_decimal"]])
+    assert np.all(np.abs(P - want) <= 4e-16 * np.maximum(want, 1e-300)), P - want
+
+
+def _qk_inputs(rng, L, D):
+    Q = rng.standard_normal((L, D)) * rng.lognormal(0, 1, D)[None, :]
+    K = rng.standard_normal((L, D))
+    Q[:, 2] = 0.0                        # a dead feature: score 0
+    K[:, 4] = K[:, 1]
+    Q[:, 4] = Q[:, 1]                    # features 1 and 4 tie exactly
+    return Q, K
+
+
+def pin_qk_scores(lib):
+    """Feature scores equal numpy's norms of the block's query columns times
+    the norms of the candidate keys' columns; keys a block does not see change
+    nothing; the dropped scores bound the error of the reduced logits; the kept
+    set matches a stable argsort and nests in r."""
+    rng = _rng(31)
+    L, D, qb = 37, 8, 12                 # blocks of 12, 12, 12, 1 queries
+    Q, K = _qk_inputs(rng, L, D)
+    for causal in (True, False):
+        for g in range(4):
+            q0 = g * qb
+            nq = min(qb, L - q0)
+            Kg = O.pv_prefix(L, qb, g, causal, lib)
+            s64, s32 = O.qk_scores(Q, K, q0, nq, Kg, True, lib)
+            want = np.linalg.norm(Q[q0:q0 + nq], axis=0) * np.linalg.norm(K[:Kg], axis=0)
+            assert np.allclose(s64, want, rtol=1e-14, atol=0)
+            assert np.array_equal(s32, s64.astype(np.float32))
+            a64, _ = O.qk_scores(Q, K, q0, nq, Kg, False, lib)
+            assert np.allclose(a64, np.linalg.norm(Q[q0:q0 + nq], axis=0), rtol=1e-14, atol=0)
+            # keys past the candidates and queries outside the block do not matter
+            K2 = K.copy()
+            K2[Kg:] *= 1e3
+            Q2 = Q.copy()
+            Q2[:q0] = 7.0
+            Q2[q0 + nq:] = -3.0
+            assert np.array_equal(O.qk_scores(Q2, K2, q0, nq, Kg, True, lib)[0], s64)
+            prev = None
+            for r in (0.25, 0.5, 0.75, 1.0):
+                sel = O.qk_select_block(Q, K, qb, g, r, causal, True, lib)
+                assert sel["kk"] == math.ceil(Fraction(str(r)) * D)
+                assert np.array_equal(sel["idx"], _argsort_topk(sel["s32"], sel["kk"]))
+                if prev is not None:
+                    assert set(prev) <= set(sel["idx"])
+                prev = sel["idx"]
+                # bound on the unscaled logits over the block x candidate keys
+                I = sel["idx"]
+                full = Q[q0:q0 + nq] @ K[:Kg].T
+                red = Q[q0:q0 + nq][:, I] @ K[:Kg][:, I].T
+                drop = np.setdiff1d(np.arange(D), I)
+                beta = float(np.sum(s64[drop]))
+                assert np.linalg.norm(full - red) <= beta * (1 + 1e-12) + 1e-12
+    # brute force: the kept set minimises the dropped score sum (D = 8, kk = 4)
+    s64, s32 = O.qk_scores(Q, K, 0, qb, qb, True, lib)
+    sel = O.qk_select_block(Q, K, qb, 0, 0.5, True, True, lib)
+    best = min(itertools.combinations(range(D), 4),
+               key=lambda c: (sum(float(s32[j]) for j in range(D) if j not in c), c))
+    assert tuple(sel["idx"]) == best
+
+
+def pin_attn_probs(lib):
+    """Probabilities equal scipy's softmax of numpy's masked logits (the dropped
+    features zeroed); rows sum to 1 and are 0 past the causal edge; identical
+    keys give 1/(q+1); a common shift of every key leaves P unchanged."""
+    import scipy.special as sps
+    rng = _rng(32)
+    L, D = 29, 8
+    Q, K = _qk_inputs(rng, L, D)
+    for causal in (True, False):
+        for idx in (None, np.array([0, 1, 3, 6], np.int32), np.array([5], np.int32)):
+            P = O.attn_probs(Q, K, 0, L, causal, idx, lib)
+            Qm = Q.copy()
+            if idx is not None:
+                keep = np.zeros(D, bool)
+                keep[idx] = True
+                Qm[:, ~keep] = 0.0
+            S = (Qm @ K.T) / math.sqrt(D)
+            if causal:
+                S = np.where(np.tril(np.ones((L, L), bool)), S, -np.inf)
+            want = sps.softmax(S, axis=1)
+            assert np.allclose(P, want, rtol=1e-12, atol=1e-300)
+            assert np.all(np.abs(P.sum(axis=1) - 1.0) <= 1e-14 * L)
+            if causal:
+                assert np.all(P[np.triu_indices(L, 1)] == 0.0)
+            # a block of rows in the middle equals the same rows of the whole
+            part = O.attn_probs(Q, K, 9, 7, causal, idx, lib)
+            assert np.array_equal(part, P[9:16])
+            shift = rng.standard_normal(D)
+            Ps = O.attn_probs(Q, K + shift[None, :], 0, L, causal, idx, lib)
+            assert np.allclose(Ps, P, rtol=1e-11, atol=1e-300)
+    Keq = np.tile(rng.standard_normal(D), (L, 1))
+    P = O.attn_probs(Q, Keq, 0, L, True, None, lib)
+    for q in range(L):
+        assert np.all(P[q, :q + 1] == 1.0 / (q + 1))
+
+
 ALL_PINS = [
     pin_kk_exact_rational, pin_kk_golden, pin_norms_numpy, pin_scores_numpy, pin_topk_argsort,
     pin_topk_invariants, pin_topk_bruteforce, pin_select_nesting, pin_reduced_numpy,
     pin_dense_numpy, pin_reduced_exact, pin_bound, pin_closed_forms, pin_hand_examples,
     pin_pv_numpy, pin_pv_hand, pin_q8_hand, pin_q8_rounding, pin_q8_dequant_norms,
+    pin_qk_hand, pin_qk_scores, pin_attn_probs,
 ]

@@ -50,6 +50,17 @@ MUTANTS = [
     ("q8_scale_128", "void oracle_quantize_q8", [("amax / 127.0f", "amax / 128.0f")]),
     ("q8_dequant_row_scale", "void oracle_dequant_q8", [("(double)scale[n]", "(double)scale[k % N]")]),
     ("q8_rownorm_no_scale", "void oracle_rownorms_q8", [("(double)scale[n] * (double)q", "(double)q")]),
+    ("qk_key_norm_from_queries", "void oracle_qk_scores", [("double v = K[k * D + j];", "double v = Q[k * D + j];")]),
+    ("qk_query_norm_drops_last", "void oracle_qk_scores", [("i < nq; ++i)", "i < nq - 1; ++i)")]),
+    ("qk_key_norm_no_sqrt", "void oracle_qk_scores", [("kn = sqrt(kq);", "kn = kq;")]),
+    ("qk_activation_only_ignored", "void oracle_qk_scores", [("if (use_k) {", "if (1) {")]),
+    ("qk_sum_not_product", "void oracle_qk_scores", [("double s = sqrt(qq) * kn;", "double s = sqrt(qq) + kn;")]),
+    ("probs_no_scale", "void oracle_attn_probs", [("S[k] = dot / sqrt((double)D);", "S[k] = dot;")]),
+    ("probs_scale_by_kept", "void oracle_attn_probs", [("S[k] = dot / sqrt((double)D);", "S[k] = dot / sqrt((double)nf);")]),
+    ("probs_mask_excludes_diagonal", "void oracle_attn_probs", [("causal ? q + 1 : L", "causal ? (q > 0 ? q : 1) : L")]),
+    ("probs_first_features", "void oracle_attn_probs", [("int64_t f = idx ? idx[j] : j;", "int64_t f = j;")]),
+    ("probs_unnormalised", "void oracle_attn_probs", [("p[k] /= sum;", "p[k] /= 1.0;")]),
+    ("probs_transposed_K", "void oracle_attn_probs", [("Q[q * D + f] * K[k * D + f]", "Q[q * D + f] * K[(f % L) * D + (k % D)]")]),
 ]
 
 
