@@ -249,6 +249,55 @@ int rmm_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq, c
                 const int32_t *idx, int64_t ldidx, int64_t M, int64_t N, int64_t kk, int64_t group_rows,
                 void *Y, int ydt, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- attention: the feature dimension of QK^T and the probabilities
+ * ("Escopo de Aplicacao": the method reduces the feature dimension of QK^T
+ * and, optionally, the token dimension of PV).  Q, K, V are [H][L][D] bf16
+ * (D contiguous).  Query block g holds queries q0 = g*qblock ..
+ * min(L, q0+qblock)-1; its candidate keys are k < K_g = min(L, qblock*(g+1))
+ * when causal, else every k < L.  Supported: D == 128, qblock == 128,
+ * L % 8 == 0, L <= 32768, else RMM_EUNSUPPORTED.  Q, K, V, Pt 16-byte aligned.
+ *
+ * rmm_qk_select: per (head h, block g), feature j scores
+ *   s[h][g][j] = binary32( ||Q[h][block, j]||_2 * ||K[h][0 .. K_g-1, j]||_2 )
+ * (use_k == 0: the first factor alone, the pages' activation-only rule), each
+ * norm summed in ascending order in binary64; the kk = rmm_kk(r, D) best
+ * features are kept (ties to the lower index) and written ascending to
+ * idx_out[h*G + g][0 .. kk-1], padded by repeating the last one up to
+ * rmm_kk_pad(kk).  0 < r <= 1; ldidx_out % 4 == 0, >= rmm_kk_pad(D).
+ * scores_out [H][G][D] binary32 or NULL (then the workspace holds them). */
+size_t rmm_qk_select_workspace_bytes(int64_t H, int64_t L, int64_t D, int64_t qblock, int have_scores_out);
+int rmm_qk_select(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int64_t D, double r,
+                  int64_t qblock, int causal, int use_k, int32_t *idx_out, int64_t ldidx_out,
+                  float *scores_out, void *ws, size_t ws_bytes, void *stream);
+
+/* rmm_attn_probs: the attention probabilities over the kept features,
+ *   S[q][k] = sum_{j in I(h, g)} Q[h][q][j] * K[h][k][j] / sqrt(D)
+ *   P[q][k] = exp(S[q][k] - max) / sum over the row's keys (k <= q if causal)
+ * I(h, g) = idx_qk[(h*G + g)*ldidx_qk + 0 .. kk-1], kk = rmm_kk(r_qk, D), as
+ * rmm_qk_select writes it; idx_qk == NULL: every feature (r_qk ignored).
+ * Products are exact, sums fp32; exp2 and the final rounding in binary32,
+ * stored bf16 (round to nearest even) KEY-MAJOR: Pt[h][k][q] = P[q][k] for
+ * every block's candidate keys (0 where k > q); entries past a block's
+ * candidates are not written.  Pt is [H][L][L].
+ * pv_scores [H][G][L] binary32 or NULL: for k < K_g,
+ *   pv_scores[h][g][k] = binary32( (sum over the block's queries, ascending,
+ *                                   of the stored P[q][k]) * ||V[h][k][:]||_2 )
+ * in binary64 -- the scores rmm_attn_pv forms from Pt, here without reading
+ * Pt again; V is then required.  Workspace:
+ * rmm_attn_probs_workspace_bytes(H, L, D, pv_scores != NULL) bytes. */
+size_t rmm_attn_probs_workspace_bytes(int64_t H, int64_t L, int64_t D, int have_pv_scores);
+int rmm_attn_probs(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int64_t D, int64_t qblock,
+                   int causal, const int32_t *idx_qk, int64_t ldidx_qk, double r_qk, uint16_t *Pt,
+                   const uint16_t *V, float *pv_scores, void *ws, size_t ws_bytes, void *stream);
+
+/* rmm_pv_select_scores: the kept keys of every (head, block) from the
+ * pv_scores of rmm_attn_probs, exactly as rmm_pv_select keeps them from its
+ * own scores: kk_g = rmm_kk(r, K_g) keys, ascending in idx_out[h*G + g][:],
+ * padded by repeating the last one.  0 < r < 1; ldidx_out % 4 == 0,
+ * >= rmm_kk_pad(L).  No workspace.  The product is then rmm_pv_gemm. */
+int rmm_pv_select_scores(const float *scores, int64_t H, int64_t L, double r, int64_t qblock, int causal,
+                         int32_t *idx_out, int64_t ldidx_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

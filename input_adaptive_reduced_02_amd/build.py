@@ -25,7 +25,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["rmm_api.hip", "rmm_score.hip", "rmm_select.hip", "rmm_gather.hip", "rmm_gemm.hip",
-           "rmm_pv.hip", "rmm_q8.hip"]
+           "rmm_pv.hip", "rmm_q8.hip", "rmm_attn.hip"]
 
 
 def _compile(src, objdir=OBJ, extra=(), csrc=CSRC):

@@ -318,3 +318,108 @@ int rmm_pv_gemm(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ attention producer
+namespace {
+
+bool attn_shape_supported(int64_t L, int64_t D, int64_t qblock)
+{
+    return D == 128 && qblock == 128 && L % 8 == 0 && L <= kSelectMaxK;
+}
+
+int attn_check(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int64_t D, int64_t qblock)
+{
+    if (H < 1 || L < 1 || D < 1 || qblock < 1) return RMM_EINVAL;
+    if (!Q || !K || !aligned16(Q) || !aligned16(K)) return RMM_EINVAL;
+    return RMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rmm_qk_select_workspace_bytes(int64_t H, int64_t L, int64_t D, int64_t qblock, int have_scores_out)
+{
+    if (H < 1 || L < 1 || D < 1 || qblock < 1 || have_scores_out) return 0;
+    const int64_t G = (L + qblock - 1) / qblock;
+    return align_up((size_t)H * G * D * sizeof(float));
+}
+
+int rmm_qk_select(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int64_t D, double r,
+                  int64_t qblock, int causal, int use_k, int32_t *idx_out, int64_t ldidx_out,
+                  float *scores_out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (int e = attn_check(Q, K, H, L, D, qblock)) return e;
+    if (!(r > 0.0) || !(r <= 1.0)) return RMM_EINVAL;
+    if (!idx_out || !aligned16(idx_out) || ldidx_out % 4 != 0 || ldidx_out < pad_up(D)) return RMM_EINVAL;
+    if (scores_out && !aligned4(scores_out)) return RMM_EINVAL;
+    if (!attn_shape_supported(L, D, qblock)) return RMM_EUNSUPPORTED;
+    const size_t need = rmm_qk_select_workspace_bytes(H, L, D, qblock, scores_out != nullptr);
+    if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
+    hipStream_t s = as_stream(stream);
+    const int64_t G = (L + qblock - 1) / qblock;
+    float *sc = scores_out ? scores_out : (float *)ws;
+    if (hipError_t e = launch_qk_score(Q, K, H, L, causal ? 1 : 0, use_k ? 1 : 0, sc, s)) return hip_status(e);
+    SelectShape sh{};
+    sh.groups = H * G;
+    sh.K = D;
+    sh.lds = D;
+    sh.kk = kk_rule(r, D);
+    return hip_status(launch_select(sc, sh, idx_out, ldidx_out, nullptr, nullptr, s));
+}
+
+size_t rmm_attn_probs_workspace_bytes(int64_t H, int64_t L, int64_t D, int have_pv_scores)
+{
+    (void)D;
+    if (H < 1 || L < 1 || !have_pv_scores) return 0;
+    return align_up((size_t)H * L * sizeof(double));
+}
+
+int rmm_attn_probs(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int64_t D, int64_t qblock,
+                   int causal, const int32_t *idx_qk, int64_t ldidx_qk, double r_qk, uint16_t *Pt,
+                   const uint16_t *V, float *pv_scores, void *ws, size_t ws_bytes, void *stream)
+{
+    if (int e = attn_check(Q, K, H, L, D, qblock)) return e;
+    if (!Pt || !aligned16(Pt)) return RMM_EINVAL;
+    int64_t kk = D;
+    if (idx_qk) {
+        if (!(r_qk > 0.0) || !(r_qk <= 1.0)) return RMM_EINVAL;
+        kk = kk_rule(r_qk, D);
+        if (!aligned4(idx_qk) || ldidx_qk < kk) return RMM_EINVAL;
+    }
+    if (pv_scores && (!aligned4(pv_scores) || !V || !aligned16(V))) return RMM_EINVAL;
+    if (!attn_shape_supported(L, D, qblock)) return RMM_EUNSUPPORTED;
+    const size_t need = rmm_attn_probs_workspace_bytes(H, L, D, pv_scores != nullptr);
+    if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
+    hipStream_t s = as_stream(stream);
+    double *vnorm = nullptr;
+    if (pv_scores) {
+        vnorm = (double *)ws;
+        if (hipError_t e = launch_pv_vnorm(V, H, L, D, vnorm, s)) return hip_status(e);
+    }
+    return hip_status(launch_attn_probs(Q, K, H, L, causal ? 1 : 0, idx_qk, idx_qk ? ldidx_qk : 0, kk, Pt, vnorm,
+                                        pv_scores, s));
+}
+
+int rmm_pv_select_scores(const float *scores, int64_t H, int64_t L, double r, int64_t qblock, int causal,
+                         int32_t *idx_out, int64_t ldidx_out, void *stream)
+{
+    if (H < 1 || L < 1 || qblock < 1) return RMM_EINVAL;
+    if (!scores || !aligned4(scores)) return RMM_EINVAL;
+    if (!(r > 0.0) || !(r < 1.0)) return RMM_EINVAL;
+    if (!idx_out || !aligned16(idx_out) || ldidx_out % 4 != 0 || ldidx_out < pad_up(L)) return RMM_EINVAL;
+    if (qblock != 128 || L % 8 != 0 || L > kSelectMaxK) return RMM_EUNSUPPORTED;
+    const int64_t G = (L + qblock - 1) / qblock;
+    SelectShape sh{};
+    sh.groups = H * G;
+    sh.K = L;
+    sh.lds = L;
+    sh.pv = 1;
+    sh.Gq = G;
+    sh.qblock = qblock;
+    sh.causal = causal;
+    sh.r = r;
+    return hip_status(launch_select(scores, sh, idx_out, ldidx_out, nullptr, nullptr, as_stream(stream)));
+}
+
+}  // extern "C"

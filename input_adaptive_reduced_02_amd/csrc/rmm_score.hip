@@ -300,6 +300,13 @@ k_pv_mass(const uint16_t *__restrict__ Pt, int64_t H, int64_t L, int64_t qblock,
     }
 }
 
+hipError_t launch_pv_vnorm(const uint16_t *V, int64_t H, int64_t L, int64_t D, double *vnorm, hipStream_t s)
+{
+    const int64_t HL = H * L;
+    hipLaunchKernelGGL(k_pv_vnorm, dim3((unsigned)((HL + 255) / 256)), dim3(256), 0, s, V, HL, D, vnorm);
+    return hipGetLastError();
+}
+
 hipError_t launch_pv_score(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D,
                            int64_t qblock, int causal, double *vnorm, float *scores, hipStream_t s)
 {

@@ -83,6 +83,16 @@ def _declare(L):
     L.rmm_gemm_q8_workspace_bytes.argtypes = [_L, _L, _L, _L]
     L.rmm_gemm_q8.restype = _I
     L.rmm_gemm_q8.argtypes = [_P, _L, _P, _L, _P, _P, _L, _L, _L, _L, _L, _P, _I, _L, _P, _S, _P]
+    L.rmm_qk_select_workspace_bytes.restype = _S
+    L.rmm_qk_select_workspace_bytes.argtypes = [_L, _L, _L, _L, _I]
+    L.rmm_qk_select.restype = _I
+    L.rmm_qk_select.argtypes = [_P, _P, _L, _L, _L, _Dbl, _L, _I, _I, _P, _L, _P, _P, _S, _P]
+    L.rmm_attn_probs_workspace_bytes.restype = _S
+    L.rmm_attn_probs_workspace_bytes.argtypes = [_L, _L, _L, _I]
+    L.rmm_attn_probs.restype = _I
+    L.rmm_attn_probs.argtypes = [_P, _P, _L, _L, _L, _L, _I, _P, _L, _Dbl, _P, _P, _P, _P, _S, _P]
+    L.rmm_pv_select_scores.restype = _I
+    L.rmm_pv_select_scores.argtypes = [_P, _L, _L, _Dbl, _L, _I, _P, _L, _P]
     return L
 
 
@@ -253,6 +263,49 @@ def rmm_pv_gemm(Pt, V, r, idx=None, qblock=128, causal=True, O=None, odt=torch.b
         _ptr(Pt), _ptr(V), H, L, D, float(r), qblock, int(bool(causal)), _ptr(idx), ldix, _ptr(O), _dt(O),
         _stream(V)))
     return O
+
+
+def rmm_qk_select(Q, K, r, qblock=128, causal=True, use_k=True, idx_out=None, scores_out=None, ws=None):
+    """Kept features [H*G, pad(D)] int32 of QK^T per (head, query block);
+    Q, K are [H, L, D] bf16."""
+    H, L, D = Q.shape
+    G = -(-L // qblock)
+    if idx_out is None:
+        idx_out = torch.empty((H * G, rmm_kk_pad(D)), dtype=torch.int32, device=Q.device)
+    need = int(lib().rmm_qk_select_workspace_bytes(H, L, D, qblock, int(scores_out is not None)))
+    w = _ws(need, Q.device, ws)
+    _check("rmm_qk_select", lib().rmm_qk_select(
+        _ptr(Q), _ptr(K), H, L, D, float(r), qblock, int(bool(causal)), int(bool(use_k)), _ptr(idx_out),
+        idx_out.stride(0), _ptr(scores_out), _ptr(w), need, _stream(Q)))
+    return idx_out
+
+
+def rmm_attn_probs(Q, K, idx_qk=None, r_qk=1.0, qblock=128, causal=True, Pt=None, V=None, pv_scores=None,
+                   ws=None):
+    """Key-major attention probabilities Pt [H, L, L] bf16 over the kept
+    features idx_qk (None: all); with V and pv_scores [H, G, L] float32 also
+    the P.V key scores."""
+    H, L, D = Q.shape
+    if Pt is None:
+        Pt = torch.empty((H, L, L), dtype=torch.bfloat16, device=Q.device)
+    need = int(lib().rmm_attn_probs_workspace_bytes(H, L, D, int(pv_scores is not None)))
+    w = _ws(need, Q.device, ws)
+    ldix = idx_qk.stride(0) if idx_qk is not None else 0
+    _check("rmm_attn_probs", lib().rmm_attn_probs(
+        _ptr(Q), _ptr(K), H, L, D, qblock, int(bool(causal)), _ptr(idx_qk), ldix, float(r_qk), _ptr(Pt),
+        _ptr(V), _ptr(pv_scores), _ptr(w), need, _stream(Q)))
+    return Pt
+
+
+def rmm_pv_select_scores(scores, r, qblock=128, causal=True, idx_out=None):
+    """Kept-key lists [H*G, pad(L)] int32 from rmm_attn_probs' P.V scores [H, G, L]."""
+    H, G, L = scores.shape
+    if idx_out is None:
+        idx_out = torch.empty((H * G, rmm_kk_pad(L)), dtype=torch.int32, device=scores.device)
+    _check("rmm_pv_select_scores", lib().rmm_pv_select_scores(
+        _ptr(scores), H, L, float(r), qblock, int(bool(causal)), _ptr(idx_out), idx_out.stride(0),
+        _stream(scores)))
+    return idx_out
 
 
 def rmm_quantize_q8(B, Bq=None, scale=None):

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 22, names
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -187,3 +187,31 @@ def test_validation_rejects_bad_arguments():
     assert need == 112 * 2 * 64 * 256 * 4 + 112 * 4
     assert L.rmm_gemm_q8_workspace_bytes(2048, 4096, 4096, 128) == 0            # 512 tiles: no split
     assert L.rmm_gemm_q8(P, 64, P2, 32, P3, None, 0, 64, 32, 64, 64, P3, BF, 32, P3, 16, None) == EINVAL   # short ws
+    # qk_select(Q, K, H, L, D, r, qblock, causal, use_k, idx, ldidx, scores, ws, wsb, stream)
+    QW = L.rmm_qk_select_workspace_bytes(2, 256, 128, 128, 0)
+    assert QW == 2 * 2 * 128 * 4
+    assert L.rmm_qk_select_workspace_bytes(2, 256, 128, 128, 1) == 0
+    assert L.rmm_qk_select(None, P2, 2, 256, 128, 0.5, 128, 1, 1, P3, 128, None, P3, QW, None) == EINVAL
+    assert L.rmm_qk_select(P, P2, 2, 256, 128, 0.0, 128, 1, 1, P3, 128, None, P3, QW, None) == EINVAL    # r
+    assert L.rmm_qk_select(P, P2, 2, 256, 128, nan, 128, 1, 1, P3, 128, None, P3, QW, None) == EINVAL
+    assert L.rmm_qk_select(P, P2, 2, 256, 128, 0.5, 128, 1, 1, P3, 64, None, P3, QW, None) == EINVAL     # ldidx < pad(D)
+    assert L.rmm_qk_select(P, P2, 2, 256, 128, 0.5, 128, 1, 1, None, 128, None, P3, QW, None) == EINVAL  # no idx
+    assert L.rmm_qk_select(P, P2, 2, 256, 128, 0.5, 128, 1, 1, P3, 128, None, P3, 16, None) == EINVAL    # short ws
+    assert L.rmm_qk_select(P, P2, 2, 256, 64, 0.5, 128, 1, 1, P3, 128, None, P3, QW, None) == EUNSUP     # D
+    assert L.rmm_qk_select(P, P2, 2, 256, 128, 0.5, 64, 1, 1, P3, 128, None, P3, 1 << 20, None) == EUNSUP  # qblock
+    # attn_probs(Q, K, H, L, D, qblock, causal, idx, ldidx, r_qk, Pt, V, pv_scores, ws, wsb, stream)
+    AW = L.rmm_attn_probs_workspace_bytes(2, 256, 128, 1)
+    assert AW == 2 * 256 * 8 and L.rmm_attn_probs_workspace_bytes(2, 256, 128, 0) == 0
+    assert L.rmm_attn_probs(P, P2, 2, 256, 128, 128, 1, None, 0, 1.0, None, None, None, None, 0, None) == EINVAL  # Pt
+    assert L.rmm_attn_probs(P, MIS, 2, 256, 128, 128, 1, None, 0, 1.0, P3, None, None, None, 0, None) == EINVAL
+    assert L.rmm_attn_probs(P, P2, 2, 256, 128, 128, 1, P3, 128, 0.0, P3, None, None, None, 0, None) == EINVAL  # r_qk
+    assert L.rmm_attn_probs(P, P2, 2, 256, 128, 128, 1, P3, 32, 0.5, P3, None, None, None, 0, None) == EINVAL   # ldidx < kk
+    assert L.rmm_attn_probs(P, P2, 2, 256, 128, 128, 1, None, 0, 1.0, P3, None, P3, P3, AW, None) == EINVAL     # no V
+    assert L.rmm_attn_probs(P, P2, 2, 256, 128, 128, 1, None, 0, 1.0, P3, P, P3, P3, 8, None) == EINVAL         # short ws
+    assert L.rmm_attn_probs(P, P2, 2, 252, 128, 128, 1, None, 0, 1.0, P3, None, None, None, 0, None) == EUNSUP  # L % 8
+    # pv_select_scores(scores, H, L, r, qblock, causal, idx, ldidx, stream)
+    assert L.rmm_pv_select_scores(None, 2, 256, 0.5, 128, 1, P3, 256, None) == EINVAL
+    assert L.rmm_pv_select_scores(P, 2, 256, 1.0, 128, 1, P3, 256, None) == EINVAL     # r == 1
+    assert L.rmm_pv_select_scores(P, 2, 256, 0.5, 128, 1, P3, 128, None) == EINVAL     # ldidx < pad(L)
+    assert L.rmm_pv_select_scores(P, 2, 256, 0.5, 128, 1, MIS, 256, None) == EINVAL
+    assert L.rmm_pv_select_scores(P, 2, 256, 0.5, 64, 1, P3, 256, None) == EUNSUP
