@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="attn_proj",
-                   choices=["attn_proj", "mlp_down", "decode", "decode_q8", "pv4k", "pv16k", "tiny"])
+                   choices=["attn_proj", "mlp_down", "decode", "decode_q8", "pv4k", "pv16k", "attn4k", "tiny"])
     p.add_argument("--ratios", type=str, default=None, help="comma-separated r values")
     p.add_argument("--headline-r", type=float, default=0.5)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -261,15 +261,115 @@ class PV:
                            f"reduced P.V, {fl / 1e9:.2f} GFLOP in {dt:.1f} s", seconds=round(dt, 2))
 
 
+class Attn:
+    """Causal attention with both attention-side reductions: QK^T over the kept
+    features of each 128-query block (the probabilities producer), then P.V
+    over the kept keys chosen from the scores the producer emits.  32 heads,
+    head dim 128.  One r for both reductions; r = 1 is the dense producer and
+    the dense causal P.V."""
+
+    def __init__(self, L, dev):
+        import torch
+        from input_adaptive_reduced_02_amd import rmm, synth
+        self.rmm, self.torch = rmm, torch
+        self.H, self.L, self.D = 32, L, 128
+        self.copies = 1
+        self.name = f"attn{L // 1024}k"
+        self.ratios = synth.RATIOS["pv"]
+        self.dev = dev
+        self.G = L // 128
+        q, k, v = synth.pv_qkv(self.H, L, self.D)
+        self.q_bits, self.k_bits, self.v_bits = q, k, v
+        up = lambda b: torch.from_numpy(b.view("int16")).view(torch.bfloat16).to(dev)
+        self.Q, self.K, self.V = up(q), up(k), up(v)
+        self.Pt = torch.empty((self.H, L, L), dtype=torch.bfloat16, device=dev)
+        self.pvs = torch.empty((self.H, self.G, L), dtype=torch.float32, device=dev)
+        self.idx_qk = torch.empty((self.H * self.G, rmm.rmm_kk_pad(self.D)), dtype=torch.int32, device=dev)
+        self.idx_pv = torch.empty((self.H * self.G, rmm.rmm_kk_pad(L)), dtype=torch.int32, device=dev)
+        self.O = torch.empty((self.H, L, self.D), dtype=torch.bfloat16, device=dev)
+        self.qs = torch.empty((self.H, self.G, self.D), dtype=torch.float32, device=dev)
+        need = int(rmm.lib().rmm_attn_probs_workspace_bytes(self.H, L, self.D, 1))
+        self.wsp = torch.empty(need, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def describe(self, r):
+        return (f"{self.name}: causal attention producer (QK^T over kept features, softmax, key-major P, "
+                f"P.V key scores) + P.V over kept keys, {self.H} heads, L={self.L}, head dim {self.D}, bf16, "
+                f"128-query blocks, r={r} for both")
+
+    def _kks(self, r):
+        return [self.rmm.rmm_kk(r, min(self.L, 128 * (g + 1))) for g in range(self.G)]
+
+    def stages(self, r):
+        rmm = self.rmm
+        if r >= 1.0:
+            return [("probs", lambda: rmm.rmm_attn_probs(self.Q, self.K, None, 1.0, Pt=self.Pt)),
+                    ("gemm", lambda: rmm.rmm_pv_gemm(self.Pt, self.V, 1.0, None, O=self.O))], self.D
+        return [("score", lambda: rmm.rmm_qk_select(self.Q, self.K, r, idx_out=self.idx_qk, scores_out=self.qs)),
+                ("probs", lambda: rmm.rmm_attn_probs(self.Q, self.K, self.idx_qk, r, Pt=self.Pt, V=self.V,
+                                                     pv_scores=self.pvs, ws=self.wsp)),
+                ("select", lambda: rmm.rmm_pv_select_scores(self.pvs, r, idx_out=self.idx_pv)),
+                ("gemm", lambda: rmm.rmm_pv_gemm(self.Pt, self.V, r, self.idx_pv, O=self.O))], \
+            self.rmm.rmm_kk(r, self.D)
+
+    roof_stage = "probs"
+
+    def flops(self, r):
+        """The method's retained work, each product counted once: QK^T over
+        the kept features on the causal prefixes, P.V over the kept keys."""
+        kq = self.rmm.rmm_kk(r, self.D)
+        qk = sum(2.0 * 128 * min(self.L, 128 * (g + 1)) * kq for g in range(self.G)) * self.H
+        pv = sum(2.0 * 128 * kk * self.D for kk in self._kks(r)) * self.H
+        return qk + pv
+
+    def gemm_bytes(self, r):
+        """Algorithmic HBM bytes of one producer launch: Q and K read once, the
+        causal half of Pt written, and (r < 1) the P.V scores written and the
+        V norms read once."""
+        pt = sum(128 * min(self.L, 128 * (g + 1)) * 2.0 for g in range(self.G)) * self.H
+        qk = 2.0 * 2 * self.H * self.L * self.D
+        extra = 0.0
+        if r < 1.0:
+            extra = sum(min(self.L, 128 * (g + 1)) * 4.0 for g in range(self.G)) * self.H + 8.0 * self.H * self.L
+        return pt + qk + extra
+
+    bound = property(lambda self: "hbm")
+    kernel = "rmm::k_attn_probs"
+    profile_prefix = "k_attn_probs"
+
+    def cpu_baseline(self, r, groups):
+        import numpy as np
+
+        import oracle as O
+        Q0, K0, V0 = (O.widen_bf16(x[0]) for x in (self.q_bits, self.k_bits, self.v_bits))
+        fl = 0.0
+        t0 = time.perf_counter()
+        for g in range(self.G - 1, max(-1, self.G - 1 - groups), -1):
+            sel = O.qk_select_block(Q0, K0, 128, g, r, True, True)
+            P = O.attn_probs(Q0, K0, g * 128, 128, True, sel["idx"])
+            Kg = min(self.L, 128 * (g + 1))
+            Ptb = np.ascontiguousarray(P[:, :Kg].T)
+            s64, s32 = O.pv_scores(Ptb, V0[:Kg])
+            kk = O.kk(r, Kg)
+            O.pv_block(Ptb, V0[:Kg], O.topk(s32, kk))
+            fl += 2.0 * 128 * Kg * sel["kk"] + 2.0 * 128 * kk * self.D
+        dt = time.perf_counter() - t0
+        return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
+                    sample=f"{groups} query blocks of head 0 (the last ones) at r={r}: feature scores + select + "
+                           f"probabilities + key scores + select + reduced P.V, {fl / 1e9:.2f} GFLOP in {dt:.1f} s",
+                    seconds=round(dt, 2))
+
+
 def torch_int16(torch):
     return torch.int16
 
 
 # ------------------------------------------------------------------ timing
-def time_stages(torch, stages, steps, warmup):
+def time_stages(torch, stages, steps, warmup, roof_stage=None):
     """Warm up, then time `steps` whole steps (no events inside); in a second
     pass, each stage with events on the launch stream around it; in a third,
-    `steps` launches of the last stage (the GEMM) back to back between two
+    `steps` launches of the roofline stage (the last one, the GEMM, unless the
+    workload names another) back to back between two
     events, which is the kernel's own duration plus the small gap between
     queued launches (events around a single launch add its launch latency).
     Returns (ms_per_step, {stage: mean ms}, gemm ms per back-to-back launch)."""
@@ -298,7 +398,7 @@ def time_stages(torch, stages, steps, warmup):
     per = {}
     for j, (name, _) in enumerate(stages):
         per[name] = sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
-    gemm = stages[-1][1]
+    gemm = dict(stages)[roof_stage] if roof_stage else stages[-1][1]
     torch.cuda.synchronize()
     e0.record(s)
     for _ in range(steps):
@@ -314,10 +414,13 @@ GEMM_SOURCES = {
     "linear": ["rmm_gemm.hip", "rmm_gemm_dl.h", "rmm_gemm_sk.h", "rmm_tile.h", "rmm_internal.h"],
     "pv": ["rmm_pv.hip", "rmm_tile.h", "rmm_internal.h"],
     "q8": ["rmm_q8.hip", "rmm_gemm_dl.h", "rmm_tile.h", "rmm_internal.h"],
+    "attn": ["rmm_attn.hip", "rmm_tile.h", "rmm_internal.h"],
 }
 
 
 def source_family(workload):
+    if workload.startswith("attn") and workload != "attn_proj":
+        return "attn"
     return "pv" if workload.startswith("pv") else "q8" if workload.endswith("_q8") else "linear"
 
 
@@ -331,11 +434,12 @@ def gemm_source_hash(family="linear"):
     return h.hexdigest()
 
 
-def measured_traffic(workload, r):
-    """HBM bytes per GEMM launch from the committed counter summary of this
-    workload and ratio (profiles/k_gemm_<workload>_r<r>_traffic.txt), or None
-    when there is none or the GEMM sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"k_gemm_{workload}_r{r}_traffic.txt")
+def measured_traffic(workload, r, prefix="k_gemm"):
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    summary of this workload and ratio (profiles/<prefix>_<workload>_r<r>_traffic.txt,
+    prefix the kernel's name), or None when there is none or the kernel's
+    sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{workload}_r{r}_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -433,6 +537,8 @@ def main():
         copy_calibration(torch, args.copy_calibration, dev)
     if args.workload in ("pv4k", "pv16k"):
         W = PV(4096 if args.workload == "pv4k" else 16384, dev)
+    elif args.workload == "attn4k":
+        W = Attn(4096, dev)
     else:
         W = Linear(args.workload, dev)
     ratios = [float(x) for x in args.ratios.split(",")] if args.ratios else list(W.ratios)
@@ -443,7 +549,7 @@ def main():
     per_r = {}
     for r in ratios:
         stages, kk = W.stages(r)
-        ms_step, per, gemm_ms = time_stages(torch, stages, args.steps, args.warmup)
+        ms_step, per, gemm_ms = time_stages(torch, stages, args.steps, args.warmup, getattr(W, "roof_stage", None))
         fl = W.flops(r)
         per_r[r] = dict(kk=kk, ms_per_step=ms_step, stage_ms=per, gemm_ms=gemm_ms,
                         step_tflops=fl / (ms_step * 1e-3) / 1e12,
@@ -451,7 +557,8 @@ def main():
                         gemm_gbs=W.gemm_bytes(r) / (gemm_ms * 1e-3) / 1e9)
         log(f"[bench] r={r}: kk={kk} step {ms_step * 1e3:.1f} us, stages "
             + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in per.items())
-            + f"; gemm back to back {gemm_ms * 1e3:.1f} us, {per_r[r]['gemm_tflops']:.1f} TFLOP/s "
+            + f"; {getattr(W, 'roof_stage', 'gemm')} back to back {gemm_ms * 1e3:.1f} us, "
+            f"{per_r[r]['gemm_tflops']:.1f} TFLOP/s "
             f"{per_r[r]['gemm_gbs']:.0f} GB/s")
         del stages
     base = per_r[1.0]
@@ -465,12 +572,12 @@ def main():
         achieved = W.flops(headline) / (gemm_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4),
-                    traffic=measured_traffic(W.name, headline))
+                    traffic=measured_traffic(W.name, headline, getattr(W, "profile_prefix", "k_gemm")))
     else:
         achieved = W.gemm_bytes(headline) / (gemm_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4),
-                    traffic=measured_traffic(W.name, headline))
+                    traffic=measured_traffic(W.name, headline, getattr(W, "profile_prefix", "k_gemm")))
     roof["kernel"] = W.kernel
     roof["kernel_ms"] = round(gemm_ms, 5)
 
@@ -479,7 +586,7 @@ def main():
         groups = args.cpu_groups
         if groups is None:
             groups = {"attn_proj": 24, "mlp_down": 1, "decode": 1, "decode_q8": 1, "tiny": 1, "pv4k": 8,
-                      "pv16k": 2}[W.name]
+                      "pv16k": 2, "attn4k": 32}[W.name]
         log(f"[bench] oracle baseline on {groups} groups ...")
         cpu = W.cpu_baseline(headline, groups)
         log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s ({cpu['seconds']} s)")

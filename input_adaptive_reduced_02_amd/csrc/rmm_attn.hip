@@ -16,13 +16,15 @@
 // the token-dimension selection needs no second pass over P.
 //
 // k_attn_probs, one 512-thread workgroup per (head, query block):
-//   waves 0-3 (compute) hold the block's 128 queries x KP kept features as
-//   MFMA fragments in registers for the whole kernel and multiply them with
-//   key tiles of 128 keys x KP features in LDS (v_mfma_f32_32x32x16_bf16, a
-//   2 x 2 arrangement of 64 x 64 wave tiles);
-//   waves 4-7 (helpers) stage the next key tile (16-byte loads; with a
-//   feature list, each kept feature is written to its slot so tiles are
-//   compact), and in the second pass store the finished P tile to HBM and sum
+//   waves 0-3 (compute) hold the block's 128 queries x 128 features as MFMA
+//   fragments in registers for the whole kernel, the dropped features zeroed
+//   (their products are exact zeros, so the sums are the reduced logits), and
+//   multiply them with key tiles of 128 keys in LDS (v_mfma_f32_32x32x16_bf16,
+//   a 2 x 2 arrangement of 64 x 64 wave tiles).  Compacting the kept features
+//   would save MFMA work, which does not bound this kernel (below), and costs
+//   scattered 2-byte LDS writes for every key tile;
+//   waves 4-7 (helpers) stage the next key tile (16-byte loads and LDS
+//   writes), and in the second pass store the finished P tile to HBM and sum
 //   its key rows for the P.V scores, while the compute waves work on the next
 //   tile.  One barrier per tile; key tiles and P tiles are double-buffered.
 //   Pass 1 (S^T = K Q^T, keys as rows): every lane keeps a running max and
@@ -30,11 +32,14 @@
 //   of the two key halves are merged at the end of the pass.
 //   Pass 2 (S = Q K^T, queries as rows): recompute the tile, P =
 //   exp2(S * log2(e)/sqrt(D) - M_q) with M_q = max + log2(sum) of the row,
-//   rounded to bf16; four consecutive queries of one key land in one 8-byte
-//   LDS write of the key-major tile.
-// Roofline: pass 2 writes the causal half of Pt (L^2 H bytes at L per head)
-// and both passes recompute the logits, so HBM writes and the exp2 work bound
-// the kernel; the key tiles come from L2 (a head's workgroups share an XCD).
+//   rounded to bf16 (v_cvt_pk_bf16_f32); four consecutive queries of one key
+//   land in one 8-byte LDS write of the key-major tile.  Masks are applied on
+//   the diagonal and ragged tiles only.
+// Roofline: pass 2 writes the causal half of Pt (L^2 H bytes for H heads of
+// length L) and each element costs two exp2 (one per pass), so the exp2/VALU
+// work and the HBM writes bound the kernel; the MFMA work (2 x 2 L^2 D H / 2
+// FLOP) is a small share; key tiles come from L2 (a head's workgroups share
+// an XCD).
 #include "rmm_internal.h"
 #include "rmm_tile.h"
 
@@ -47,84 +52,129 @@ constexpr int kPitch = 136;              // LDS row pitch in bf16 (272 bytes: ro
 constexpr int kTile = 128 * kPitch;      // bf16 per LDS tile
 constexpr int kAttnThreads = 512;
 
-// ------------------------------------------------------------------ feature scores
-// acc += x*x over rows t0 .. t1-1 of a column with row stride kHD, ascending
-// (16 loads in flight; fma of an exact square rounds once, like x*x + acc).
-__device__ __forceinline__ void sumsq_col(const uint16_t *p, int64_t t0, int64_t t1, double &acc)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
+
+// two binary32 values -> packed bf16 (v_cvt_pk_bf16_f32: round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 {
-    int64_t t = t0;
-    for (; t + 16 <= t1; t += 16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// ------------------------------------------------------------------ feature scores
+// One 256-thread workgroup per head.  Lane j < 128 carries the key column j's
+// running sum of squares through the rows in order (its value at the end of
+// block g's prefix is that block's key norm squared); lane 128 + j sums the
+// squares of query column j over the current block.  The sums must run in
+// ascending row order in binary64 (each fma of an exact square rounds once,
+// like acc + x*x), so each is one dependent chain; to keep the chains fed,
+// 128-row tiles of Q and K are staged in LDS with 16-byte loads, the next
+// tile's loads in flight while the chains consume the current one.
+// scores[h][g][j] = binary32(sqrt(qsum) * sqrt(ksum)).
+constexpr int kScoreThreads = 256;
+
+// acc += x*x for rows 0 .. rows-1 of column j of an LDS tile (row stride kHD), in order
+__device__ __forceinline__ void chain_tile(const uint16_t *t, int j, int rows, double &acc)
+{
+    int r = 0;
+    for (; r + 16 <= rows; r += 16) {
         double x[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) x[u] = (double)bf16_to_f32(p[(t + u) * kHD]);
+        for (int u = 0; u < 16; ++u) x[u] = (double)bf16_to_f32(t[(r + u) * kHD + j]);
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc = __builtin_fma(x[u], x[u], acc);
     }
-    for (; t < t1; ++t) {
-        const double x = (double)bf16_to_f32(p[t * kHD]);
+    for (; r < rows; ++r) {
+        const double x = (double)bf16_to_f32(t[r * kHD + j]);
         acc = __builtin_fma(x, x, acc);
     }
 }
 
-// the same over two columns at once (query and key feature j)
-__device__ __forceinline__ void sumsq_cols2(const uint16_t *p, const uint16_t *q, int64_t t0, int64_t t1,
-                                            double &a, double &b)
-{
-    int64_t t = t0;
-    for (; t + 16 <= t1; t += 16) {
-        double x[16], y[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            x[u] = (double)bf16_to_f32(p[(t + u) * kHD]);
-            y[u] = (double)bf16_to_f32(q[(t + u) * kHD]);
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            a = __builtin_fma(x[u], x[u], a);
-            b = __builtin_fma(y[u], y[u], b);
-        }
-    }
-    for (; t < t1; ++t) {
-        const double x = (double)bf16_to_f32(p[t * kHD]), y = (double)bf16_to_f32(q[t * kHD]);
-        a = __builtin_fma(x, x, a);
-        b = __builtin_fma(y, y, b);
-    }
-}
-
-// One lane per (head, feature j) walks the rows in order: the key column's
-// running sum of squares is the prefix norm of every block in turn, so one
-// pass gives all blocks.  scores[h][g][j], binary32 of the fp64 product.
 template <int CAUSAL, int USE_K>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(kScoreThreads)
 k_qk_score(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int64_t L, float *__restrict__ scores)
 {
-    const int64_t h = blockIdx.x >> 1;
-    const int j = (int)((blockIdx.x & 1) << 6) + (int)threadIdx.x;
-    const uint16_t *qp = Q + h * L * kHD + j;
-    const uint16_t *kp = K + h * L * kHD + j;
+    __shared__ __attribute__((aligned(16))) uint16_t qs[2][kQB * kHD];
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2][kQB * kHD];
+    __shared__ double qn[kHD];
+    const int64_t h = blockIdx.x;
+    const int tid = threadIdx.x, j = tid & 127;
+    const bool klane = tid < 128;
     const int64_t G = (L + kQB - 1) / kQB;
-    float *out = scores + h * G * kHD + j;
+    const uint16_t *Qh = Q + h * L * kHD;
+    const uint16_t *Kh = K + h * L * kHD;
+    float *out = scores + h * G * kHD;
+    // tile t of a [L][128] matrix: 2048 16-byte chunks, 8 per thread
+    auto load = [&](const uint16_t *M, int64_t t, u32x4 (&v)[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + kScoreThreads * i;
+            const int64_t row = t * kQB + (c >> 4);
+            v[i] = row < L ? *(const u32x4 *)(M + row * kHD + 8 * (c & 15)) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store = [&](uint16_t *buf, const u32x4 (&v)[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + kScoreThreads * i;
+            *(u32x4 *)(buf + (c >> 4) * kHD + 8 * (c & 15)) = v[i];
+        }
+    };
+    auto rows_of = [&](int64_t t) { return (int)((L - t * kQB < kQB) ? (L - t * kQB) : kQB); };
+    u32x4 vq[8], vk[8];
+
     double kfull = 1.0;
     if (USE_K && !CAUSAL) {
-        double a = 0.0;
-        sumsq_col(kp, 0, L, a);
-        kfull = __builtin_sqrt(a);
+        // the whole key column first: one chain over every tile
+        load(Kh, 0, vk);
+        double ka = 0.0;
+        for (int64_t t = 0; t < G; ++t) {
+            __syncthreads();
+            store(ks[t & 1], vk);
+            __syncthreads();
+            if (t + 1 < G) load(Kh, t + 1, vk);
+            if (klane) chain_tile(ks[t & 1], j, rows_of(t), ka);
+        }
+        kfull = __builtin_sqrt(ka);
     }
+
+    load(Qh, 0, vq);
+    if (USE_K && CAUSAL) load(Kh, 0, vk);
     double ka = 0.0;
     for (int64_t g = 0; g < G; ++g) {
-        const int64_t t0 = g * kQB, t1 = (t0 + kQB < L) ? t0 + kQB : L;
-        double qa = 0.0;
-        if (USE_K && CAUSAL) sumsq_cols2(qp, kp, t0, t1, qa, ka);
-        else sumsq_col(qp, t0, t1, qa);
-        const double kn = USE_K ? (CAUSAL ? __builtin_sqrt(ka) : kfull) : 1.0;
-        out[g * kHD] = (float)(__builtin_sqrt(qa) * kn);
+        __syncthreads();                 // the previous step's readers are done
+        store(qs[g & 1], vq);
+        if (USE_K && CAUSAL) store(ks[g & 1], vk);
+        __syncthreads();
+        if (g + 1 < G) {
+            load(Qh, g + 1, vq);
+            if (USE_K && CAUSAL) load(Kh, g + 1, vk);
+        }
+        const int rows = rows_of(g);
+        if (!klane) {
+            double qa = 0.0;
+            chain_tile(qs[g & 1], j, rows, qa);
+            qn[j] = __builtin_sqrt(qa);
+        } else if (USE_K && CAUSAL) {
+            chain_tile(ks[g & 1], j, rows, ka);
+        }
+        __syncthreads();
+        if (klane) {
+            const double kn = USE_K ? (CAUSAL ? __builtin_sqrt(ka) : kfull) : 1.0;
+            out[g * kHD + j] = (float)(qn[j] * kn);
+        }
     }
 }
 
 hipError_t launch_qk_score(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int causal, int use_k,
                            float *scores, hipStream_t s)
 {
-    dim3 grid((unsigned)(2 * H)), block(64);
+    dim3 grid((unsigned)H), block(kScoreThreads);
     if (causal && use_k) hipLaunchKernelGGL((k_qk_score<1, 1>), grid, block, 0, s, Q, K, L, scores);
     else if (use_k) hipLaunchKernelGGL((k_qk_score<0, 1>), grid, block, 0, s, Q, K, L, scores);
     else hipLaunchKernelGGL((k_qk_score<0, 0>), grid, block, 0, s, Q, K, L, scores);
@@ -132,40 +182,12 @@ hipError_t launch_qk_score(const uint16_t *Q, const uint16_t *K, int64_t H, int6
 }
 
 // ------------------------------------------------------------------ probabilities
-// Window w of a row is its features 8w .. 8w+7 (one 16-byte chunk).  A
-// staging thread always handles the same window; `mask` marks its kept
-// features and `base` is the slot of the first of them (the number of kept
-// features below 8w).
-struct Window {
-    uint32_t mask;
-    int base;
-};
-
-template <int IDX>
-__device__ __forceinline__ void put_chunk(uint16_t *row, int w, const Window &win, u32x4 v)
-{
-    if (!IDX) {
-        *(u32x4 *)(row + 8 * w) = v;
-        return;
-    }
-    int s = win.base;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        if ((win.mask >> e) & 1u) {
-            const uint32_t word = v[e >> 1];
-            row[s] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
-            ++s;
-        }
-    }
-}
-
 __device__ __forceinline__ u32x4 load_chunk(const uint16_t *base, int64_t row, int64_t rows_valid, int w)
 {
     if (row < rows_valid) return *(const u32x4 *)(base + row * kHD + 8 * w);
     return u32x4{0u, 0u, 0u, 0u};
 }
 
-template <int IDX, int KS>
 __global__ void __launch_bounds__(kAttnThreads)
 k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int64_t H, int64_t L, int causal,
              const int32_t *__restrict__ idx, int64_t ldidx, int kk, uint16_t *__restrict__ Pt,
@@ -191,35 +213,32 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
     const uint16_t *Kh = K + h * L * kHD;
     const float c2 = 1.4426950408889634f / 11.313708498984761f;   // log2(e) / sqrt(128)
 
-    // ---- this thread's feature window and its kept features
+    // ---- this thread's 16-byte window (features 8w .. 8w+7 of a row) and, with
+    // a feature list, the mask that zeroes its dropped features in the query
+    // tile: a dropped feature then adds exact zeros to every logit, so the
+    // key tiles need no change
     const int w = tid & 15;
-    Window win{0xffu, 8 * w};
-    if (IDX) {
+    u32x4 keep = {~0u, ~0u, ~0u, ~0u};
+    if (idx) {
         const int32_t *I = idx + (h * G + g) * ldidx;
         uint32_t m = 0;
-        int b = 0;
         for (int j = 0; j < kk; ++j) {
             const int f = I[j];
             if ((f >> 3) == w) m |= 1u << (f & 7);
-            b += f < 8 * w;
         }
-        win.mask = m;
-        win.base = b;
-        // pad slots kk .. KP-1 of every row of both key buffers and the query
-        // tile stay zero (staging writes only slots below kk)
-        for (int r = tid; r < 3 * 128; r += kAttnThreads) {
-            uint16_t *row = (r < 256) ? &kbuf[r >> 7][(r & 127) * kPitch] : &pbuf[0][(r & 127) * kPitch];
-            for (int s = kk; s < 16 * KS; ++s) row[s] = 0;
-        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            keep[e] = (((m >> (2 * e)) & 1u) ? 0x0000ffffu : 0u) | (((m >> (2 * e + 1)) & 1u) ? 0xffff0000u : 0u);
     }
 
     // ---- prologue: query tile into pbuf[0], key tile 0 into kbuf[0]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int c = tid + kAttnThreads * i, r = c >> 4;
-        put_chunk<IDX>(&pbuf[0][r * kPitch], w, win, load_chunk(Qh, q0 + r, L, w));
-        put_chunk<IDX>(&kbuf[0][r * kPitch], w, win, load_chunk(Kh, r, L, w));
+        *(u32x4 *)&pbuf[0][r * kPitch + 8 * w] = load_chunk(Qh, q0 + r, L, w) & keep;
+        *(u32x4 *)&kbuf[0][r * kPitch + 8 * w] = load_chunk(Kh, r, L, w);
     }
+    constexpr int KS = kHD / 16;                       // 16-deep MFMA steps over the head dimension
     const int U = 2 * T;                               // tiles over both passes
     auto tile_of = [&](int u) { return u < T ? u : u - T; };
     const int64_t Kvalid = L;                          // keys at or past L do not exist
@@ -304,18 +323,21 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                             for (int v = 0; v < 16; ++v)
                                 if (i * 32 + acc_row(0, v) > thr) acc[i][j][v] = -INFINITY;
                     }
-                    float tmax = -INFINITY;
+                    float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, acc[i][j][v]);
+                        for (int v = 0; v < 16; ++v) t4[v & 3] = fmaxf(t4[v & 3], acc[i][j][v]);
+                    const float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
                     const float mn = fmaxf(m_run[j], tmax * c2);
-                    float sum = 0.0f;
+                    // v_exp_f32 straight (arguments <= 0; results below 2^-126 may flush to 0)
+                    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) sum += exp2f(acc[i][j][v] * c2 - mn);
-                    l_run[j] = l_run[j] * exp2f(m_run[j] - mn) + sum;
+                        for (int v = 0; v < 16; ++v)
+                            s4[v & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][v], c2, -mn));
+                    l_run[j] = l_run[j] * exp2f(m_run[j] - mn) + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
                     m_run[j] = mn;
                 }
             } else {
@@ -333,32 +355,37 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[i][ks], kf[j], acc[i][j], 0, 0, 0);
                 }
                 uint16_t *pb = pbuf[u & 1];
+                // P = exp2(S c2 - M_q), bf16; masked entries only on edge tiles
+                auto epilogue = [&](auto masked) {
+                    constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int kl = wk * 64 + j * 32 + (lane & 31);
-                    // query ql = qb + c with c = i*32 + acc_row(0, v) a constant;
-                    // cut when the key is past the end, or (causal) c < thr
-                    const int qb = wq * 64 + (lane >> 5) * 4;
-                    const bool gone = kl >= klim;
-                    const int thr = causal ? kl - qb - dq : -1;
+                    for (int j = 0; j < 2; ++j) {
+                        const int kl = wk * 64 + j * 32 + (lane & 31);
+                        // query ql = qb + c with c = i*32 + acc_row(0, v) a constant;
+                        // cut when the key is past the end, or (causal) c < thr
+                        const int qb = wq * 64 + (lane >> 5) * 4;
+                        const bool gone = kl >= klim;
+                        const int thr = causal ? kl - qb - dq : -1;
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                        for (int i = 0; i < 2; ++i)
 #pragma unroll
-                        for (int v4 = 0; v4 < 4; ++v4) {
-                            const int qw = i * 32 + acc_row(lane, 4 * v4);   // within the wave's 64 queries
-                            const float4 mq = *(const float4 *)&mrow[wave][qw];
-                            const float mv[4] = {mq.x, mq.y, mq.z, mq.w};
-                            uint32_t hb[4];
+                            for (int v4 = 0; v4 < 4; ++v4) {
+                                const int qw = i * 32 + acc_row(lane, 4 * v4);   // within the wave's 64 queries
+                                const float4 mq = *(const float4 *)&mrow[wave][qw];
+                                const float mv[4] = {mq.x, mq.y, mq.z, mq.w};
+                                float p[4];
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                float p = exp2f(acc[i][j][4 * v4 + e] * c2 - mv[e]);
-                                if (edge && (gone || i * 32 + acc_row(0, 4 * v4 + e) < thr)) p = 0.0f;
-                                hb[e] = f32_to_bf16(p);
+                                for (int e = 0; e < 4; ++e) {
+                                    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * v4 + e], c2, -mv[e]));
+                                    if (MASKED && (gone || i * 32 + acc_row(0, 4 * v4 + e) < thr)) p[e] = 0.0f;
+                                }
+                                const int ql = wq * 64 + qw;
+                                *(uint2 *)&pb[kl * kPitch + ql] = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
                             }
-                            const int ql = wq * 64 + qw;
-                            *(uint2 *)&pb[kl * kPitch + ql] = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-                        }
-                }
+                    }
+                };
+                if (edge) epilogue(Flag<true>{});
+                else epilogue(Flag<false>{});
             }
             __syncthreads();
         }
@@ -378,7 +405,7 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                 // key tile u+1 into its buffer (free since the last barrier), loads for tile u+2
                 uint16_t *kb = kbuf[(u + 1) & 1];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) put_chunk<IDX>(&kb[((ht + 256 * i) >> 4) * kPitch], w, win, kreg[i]);
+                for (int i = 0; i < 8; ++i) *(u32x4 *)&kb[((ht + 256 * i) >> 4) * kPitch + 8 * w] = kreg[i];
                 if (u + 2 < U) {
                     const int64_t kn0 = (int64_t)tile_of(u + 2) * kKT;
 #pragma unroll
@@ -423,25 +450,8 @@ hipError_t launch_attn_probs(const uint16_t *Q, const uint16_t *K, int64_t H, in
                              float *pvs, hipStream_t s)
 {
     const int64_t G = (L + kQB - 1) / kQB;
-    dim3 grid((unsigned)(H * G)), block(kAttnThreads);
-#define RMM_ATTN(I, KS_)                                                                                   \
-    hipLaunchKernelGGL((k_attn_probs<I, KS_>), grid, block, 0, s, Q, K, H, L, causal, idx, ldidx, (int)kk, Pt, \
-                       vnorm, pvs)
-    if (!idx) {
-        RMM_ATTN(0, 8);
-    } else {
-        switch ((kk + 15) / 16) {
-        case 1: RMM_ATTN(1, 1); break;
-        case 2: RMM_ATTN(1, 2); break;
-        case 3: RMM_ATTN(1, 3); break;
-        case 4: RMM_ATTN(1, 4); break;
-        case 5: RMM_ATTN(1, 5); break;
-        case 6: RMM_ATTN(1, 6); break;
-        case 7: RMM_ATTN(1, 7); break;
-        default: RMM_ATTN(1, 8); break;
-        }
-    }
-#undef RMM_ATTN
+    hipLaunchKernelGGL(k_attn_probs, dim3((unsigned)(H * G)), dim3(kAttnThreads), 0, s, Q, K, H, L, causal, idx,
+                       ldidx, (int)kk, Pt, vnorm, pvs);
     return hipGetLastError();
 }
 

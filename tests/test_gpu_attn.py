@@ -10,12 +10,13 @@ Bars:
     oracle evaluated on the probabilities the GPU stored);
   - kept feature and key sets exact outside the near-tie band;
   - probabilities within the bound derived from the arithmetic, per element:
-      |P_gpu - P_ref| <= 1.01 [ (2^-8 + e) P_ref ] + 1e-38
+      |P_gpu - P_ref| <= 1.01 [ (2^-8 + e) P_ref ] + 2^-126
     2^-8: rounding to bf16; e: relative error of the binary32 value before
     it, from the logit (fp32 sum of kk exact products:
     kk 2^-24 sum_j |q_j k_j|, times log2(e)/sqrt(128) and ln 2), the row
     statistics (at most L + 64 fp32 additions: (L + 64) 2^-24) and exp2/log2
-    (2^-20);
+    (2^-20); 2^-126: exp2 results below the binary32 normal range may flush
+    to zero;
   - entries past a block's candidate keys left untouched.
 """
 import math
@@ -62,7 +63,7 @@ def prob_bound(Pref, Qh, Kh, rows, Kg, kept, L):
     A = np.abs(Qh[rows][:, kept]) @ np.abs(Kh[:Kg][:, kept]).T
     e = (kk * 2.0 ** -24 * A) * (math.log2(math.e) / math.sqrt(D)) * math.log(2.0) \
         + (L + 64) * 2.0 ** -24 + 2.0 ** -20
-    return 1.01 * (2.0 ** -8 + e) * Pref + 1e-38
+    return 1.01 * (2.0 ** -8 + e) * Pref + 2.0 ** -126
 
 
 def check_block(q, k, v, idx_np, qs_np, Pt_np, pvs_np, h, g, L, r_qk, causal, use_k, tag,
