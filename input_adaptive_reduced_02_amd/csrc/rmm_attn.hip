@@ -287,105 +287,114 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                 }
             }
             const uint16_t *kb = kbuf[u & 1];
-            floatx16 acc[2][2];
+            // one K fragment: 8 features (chunk 2ks + lane/32) of key row r of the tile
+            auto kfrag = [&](int r, int ks) {
+                return *(const bf16x8 *)&kb[r * kPitch + 8 * (2 * ks + (lane >> 5))];
+            };
+            // Each pass is one straight block per tile kind (masked or not): the
+            // MFMAs of the second half are issued after those of the first, so
+            // the first half's exp2 work can run under them.
+            auto pass1 = [&](auto masked) {
+                constexpr bool MASKED = decltype(masked)::value;
+                // S^T = K Q^T: acc[i][j] rows = keys wk*64 + i*32 + .., cols = queries wq*64 + j*32 + ..
+                floatx16 acc[2][2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                    for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-            if (u < T) {
-                // pass 1, S^T = K Q^T: acc[i][j] rows = keys wk*64 + i*32 + .., cols = queries wq*64 + j*32 + ..
+                        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    bf16x8 kf[2];
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        kf[i] = *(const bf16x8 *)&kb[(wk * 64 + i * 32 + (lane & 31)) * kPitch + 8 * (2 * ks + (lane >> 5))];
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const bf16x8 kf = kfrag(wk * 64 + i * 32 + (lane & 31), ks);
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[j][ks], acc[i][j], 0, 0, 0);
-                }
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][ks], acc[i][j], 0, 0, 0);
+                    }
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if (edge) {
-                        // key kl = kb + c with c = i*32 + acc_row(0, v) a constant;
-                        // cut when c > thr
-                        const int ql = wq * 64 + j * 32 + (lane & 31);
-                        const int kb = wk * 64 + (lane >> 5) * 4;
-                        int thr = klim - kb - 1;
-                        if (causal) thr = min(thr, dq + ql - kb);
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                        for (int i = 0; i < 2; ++i)
+                    for (int j = 0; j < 2; ++j) {
+                        if (MASKED) {
+                            // key kl = kb + c with c = i*32 + acc_row(0, v) a constant;
+                            // cut when c > thr
+                            const int ql = wq * 64 + j * 32 + (lane & 31);
+                            const int kb0 = wk * 64 + (lane >> 5) * 4;
+                            int thr = klim - kb0 - 1;
+                            if (causal) thr = min(thr, dq + ql - kb0);
 #pragma unroll
                             for (int v = 0; v < 16; ++v)
                                 if (i * 32 + acc_row(0, v) > thr) acc[i][j][v] = -INFINITY;
-                    }
-                    float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                        }
+                        float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
                         for (int v = 0; v < 16; ++v) t4[v & 3] = fmaxf(t4[v & 3], acc[i][j][v]);
-                    const float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
-                    const float mn = fmaxf(m_run[j], tmax * c2);
-                    // v_exp_f32 straight (arguments <= 0; results below 2^-126 may flush to 0)
-                    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                        const float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+                        const float mn = fmaxf(m_run[j], tmax * c2);
+                        // v_exp_f32 straight (arguments <= 0; results below 2^-126 may flush to 0)
+                        float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                         for (int v = 0; v < 16; ++v)
                             s4[v & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][v], c2, -mn));
-                    l_run[j] = l_run[j] * exp2f(m_run[j] - mn) + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
-                    m_run[j] = mn;
-                }
-            } else {
-                // pass 2, S = Q K^T: acc[i][j] rows = queries wq*64 + i*32 + .., cols = keys wk*64 + j*32 + ..
+                        l_run[j] = l_run[j] * exp2f(m_run[j] - mn) + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
+                        m_run[j] = mn;
+                    }
+            };
+            auto pass2 = [&](auto masked) {
+                constexpr bool MASKED = decltype(masked)::value;
+                // S = Q K^T: acc[i][j] rows = queries wq*64 + i*32 + .., cols = keys wk*64 + j*32 + ..
+                floatx16 acc[2][2];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    bf16x8 kf[2];
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
-                        kf[j] = *(const bf16x8 *)&kb[(wk * 64 + j * 32 + (lane & 31)) * kPitch + 8 * (2 * ks + (lane >> 5))];
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const bf16x8 kf = kfrag(wk * 64 + j * 32 + (lane & 31), ks);
+#pragma unroll
+                        for (int i = 0; i < 2; ++i)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[i][ks], kf, acc[i][j], 0, 0, 0);
+                    }
+                // P = exp2(S c2 - M_q), bf16
+                uint16_t *pb = pbuf[u & 1];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int kl = wk * 64 + j * 32 + (lane & 31);
+                    // query ql = qb + c with c = i*32 + acc_row(0, v) a constant;
+                    // cut when the key is past the end, or (causal) c < thr
+                    const int qb = wq * 64 + (lane >> 5) * 4;
+                    const bool gone = kl >= klim;
+                    const int thr = causal ? kl - qb - dq : -1;
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
 #pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[i][ks], kf[j], acc[i][j], 0, 0, 0);
-                }
-                uint16_t *pb = pbuf[u & 1];
-                // P = exp2(S c2 - M_q), bf16; masked entries only on edge tiles
-                auto epilogue = [&](auto masked) {
-                    constexpr bool MASKED = decltype(masked)::value;
+                        for (int v4 = 0; v4 < 4; ++v4) {
+                            const int qw = i * 32 + acc_row(lane, 4 * v4);   // within the wave's 64 queries
+                            const float4 mq = *(const float4 *)&mrow[wave][qw];
+                            const float mv[4] = {mq.x, mq.y, mq.z, mq.w};
+                            float p[4];
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int kl = wk * 64 + j * 32 + (lane & 31);
-                        // query ql = qb + c with c = i*32 + acc_row(0, v) a constant;
-                        // cut when the key is past the end, or (causal) c < thr
-                        const int qb = wq * 64 + (lane >> 5) * 4;
-                        const bool gone = kl >= klim;
-                        const int thr = causal ? kl - qb - dq : -1;
-#pragma unroll
-                        for (int i = 0; i < 2; ++i)
-#pragma unroll
-                            for (int v4 = 0; v4 < 4; ++v4) {
-                                const int qw = i * 32 + acc_row(lane, 4 * v4);   // within the wave's 64 queries
-                                const float4 mq = *(const float4 *)&mrow[wave][qw];
-                                const float mv[4] = {mq.x, mq.y, mq.z, mq.w};
-                                float p[4];
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * v4 + e], c2, -mv[e]));
-                                    if (MASKED && (gone || i * 32 + acc_row(0, 4 * v4 + e) < thr)) p[e] = 0.0f;
-                                }
-                                const int ql = wq * 64 + qw;
-                                *(uint2 *)&pb[kl * kPitch + ql] = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
+                            for (int e = 0; e < 4; ++e) {
+                                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * v4 + e], c2, -mv[e]));
+                                if (MASKED && (gone || i * 32 + acc_row(0, 4 * v4 + e) < thr)) p[e] = 0.0f;
                             }
-                    }
-                };
-                if (edge) epilogue(Flag<true>{});
-                else epilogue(Flag<false>{});
+                            const int ql = wq * 64 + qw;
+                            *(uint2 *)&pb[kl * kPitch + ql] = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
+                        }
+                }
+            };
+            if (u < T) {
+                if (edge) pass1(Flag<true>{});
+                else pass1(Flag<false>{});
+            } else {
+                if (edge) pass2(Flag<true>{});
+                else pass2(Flag<false>{});
             }
             __syncthreads();
         }

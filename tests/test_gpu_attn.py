@@ -219,3 +219,23 @@ def test_full_size_sampled():
             log(f"  full h={h} g={g}")
             check_block(q[h:h + 1], k[h:h + 1], v[h:h + 1], idx_np[h * G:(h + 1) * G], qs_np[h:h + 1], Pt_np,
                         pvs_np[h:h + 1], 0, g, L, 0.5, True, True, f"full h={h}")
+
+
+def test_peaked_rows_key_sums():
+    """Queries scaled up make peaked rows whose probabilities span many
+    binary orders, down to underflow: the P.V key scores must still equal the
+    oracle's ascending binary64 sums on the stored P, and P stays within its
+    bound."""
+    H, L = 2, 384
+    q, k, v = synth.pv_qkv(H, L, D, seed=8)
+    qf = synth.bf16_bits_to_f32(q)
+    qf[:, 100:300] *= 9.0                      # logits with std ~9: P spans ~e^-60
+    q = synth.f32_to_bf16_bits(qf)
+    Qd, Kd, Vd = up_bf16(q), up_bf16(k), up_bf16(v)
+    idx, qs, Pt, pvs = run_producer(Qd, Kd, Vd, 0.5, True)
+    idx_np, qs_np, Pt_np, pvs_np = down(idx), down(qs), down(Pt), down(pvs)
+    tiny = np.count_nonzero((Pt_np & 0x7FFF) > 0) - np.count_nonzero((Pt_np & 0x7FFF) >= (88 << 7))
+    log(f"  peaked: {tiny} stored probabilities below 2^-39")
+    for h in range(H):
+        for g in range(3):
+            check_block(q, k, v, idx_np, qs_np, Pt_np, pvs_np, h, g, L, 0.5, True, True, "peaked")
