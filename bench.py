@@ -334,7 +334,7 @@ class Attn:
         return pt + qk + extra
 
     bound = property(lambda self: "hbm")
-    kernel = "rmm::k_attn_probs"
+    kernel = "rmm::k_attn_probs<1>"
     profile_prefix = "k_attn_probs"
 
     def cpu_baseline(self, r, groups):

@@ -188,6 +188,8 @@ __device__ __forceinline__ u32x4 load_chunk(const uint16_t *base, int64_t row, i
     return u32x4{0u, 0u, 0u, 0u};
 }
 
+// PVS: whether the P.V key scores are formed (pvs != NULL)
+template <int PVS>
 __global__ void __launch_bounds__(kAttnThreads)
 k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int64_t H, int64_t L, int causal,
              const int32_t *__restrict__ idx, int64_t ldidx, int kk, uint16_t *__restrict__ Pt,
@@ -427,7 +429,7 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                 const int64_t kp0 = (int64_t)(u - 1 - T) * kKT;
                 if (ht < 128) {
                     const int64_t k = kp0 + ht;
-                    if (pvs && k < Kvalid) {
+                    if (PVS && k < Kvalid) {
                         double mass = 0.0;
                         for (int c = 0; c < nq / 8; ++c) {
                             const u32x4 v = *(const u32x4 *)&pb[ht * kPitch + 8 * c];
@@ -459,8 +461,12 @@ hipError_t launch_attn_probs(const uint16_t *Q, const uint16_t *K, int64_t H, in
                              float *pvs, hipStream_t s)
 {
     const int64_t G = (L + kQB - 1) / kQB;
-    hipLaunchKernelGGL(k_attn_probs, dim3((unsigned)(H * G)), dim3(kAttnThreads), 0, s, Q, K, H, L, causal, idx,
-                       ldidx, (int)kk, Pt, vnorm, pvs);
+    if (pvs)
+        hipLaunchKernelGGL(k_attn_probs<1>, dim3((unsigned)(H * G)), dim3(kAttnThreads), 0, s, Q, K, H, L, causal,
+                           idx, ldidx, (int)kk, Pt, vnorm, pvs);
+    else
+        hipLaunchKernelGGL(k_attn_probs<0>, dim3((unsigned)(H * G)), dim3(kAttnThreads), 0, s, Q, K, H, L, causal,
+                           idx, ldidx, (int)kk, Pt, vnorm, pvs);
     return hipGetLastError();
 }
 
