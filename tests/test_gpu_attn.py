@@ -239,3 +239,36 @@ def test_peaked_rows_key_sums():
     for h in range(H):
         for g in range(3):
             check_block(q, k, v, idx_np, qs_np, Pt_np, pvs_np, h, g, L, 0.5, True, True, "peaked")
+
+
+def test_long_sequence_sampled():
+    """32 heads, L = 16384 (the longer P.V configuration), r = 0.5: feature
+    scores and kept features of sampled blocks of heads 0 and 31, their
+    probabilities and P.V key scores, and the kept keys from those scores."""
+    H, L = 32, 16384
+    log("attn long H=32 L=16384 r=0.5")
+    q, k, v, Qd, Kd, Vd = make_qkv(H, L, seed=2)
+    G = L // QB
+    qs = torch.zeros((H, G, D), dtype=torch.float32, device=DEV)
+    idx = rmm.rmm_qk_select(Qd, Kd, 0.5, QB, True, True, scores_out=qs)
+    Pt = torch.full((H, L, L), SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    pvs = torch.zeros((H, G, L), dtype=torch.float32, device=DEV)
+    rmm.rmm_attn_probs(Qd, Kd, idx, 0.5, QB, True, Pt=Pt, V=Vd, pv_scores=pvs)
+    kidx = rmm.rmm_pv_select_scores(pvs, 0.5, QB, True)
+    torch.cuda.synchronize()
+    idx_np, qs_np, pvs_np, kidx_np = down(idx), down(qs), down(pvs), down(kidx)
+    for h in (0, 31):
+        Pt_np = down(Pt[h])[None]
+        for g in (0, 77, G - 1):
+            log(f"  long h={h} g={g}")
+            check_block(q[h:h + 1], k[h:h + 1], v[h:h + 1], idx_np[h * G:(h + 1) * G], qs_np[h:h + 1], Pt_np,
+                        pvs_np[h:h + 1], 0, g, L, 0.5, True, True, f"long h={h}")
+            Kg = O.pv_prefix(L, QB, g, True)
+            s32 = pvs_np[h, g, :Kg]
+            kk = O.kk(0.5, Kg)
+            ref = O.topk(s32, kk)
+            Ptb = O.widen_bf16(Pt_np[0, :Kg, g * QB:(g + 1) * QB])
+            s64, _ = O.pv_scores(Ptb, O.widen_bf16(v[h])[:Kg])
+            compare_sets(kidx_np[h * G + g, :kk], dict(idx={g: ref}, near={g: O.near_ties(s64, s32, ref)}), g, kk,
+                         f"long keys h={h}")
+        del Pt_np
