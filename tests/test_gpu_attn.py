@@ -272,3 +272,20 @@ def test_long_sequence_sampled():
             compare_sets(kidx_np[h * G + g, :kk], dict(idx={g: ref}, near={g: O.near_ties(s64, s32, ref)}), g, kk,
                          f"long keys h={h}")
         del Pt_np
+
+
+@pytest.mark.parametrize("H,L,causal,r_qk", [(1, 8, True, 0.5), (1, 8, False, 0.001), (2, 136, True, 0.001),
+                                             (1, 136, False, 1.0), (3, 64, True, 0.3)])
+def test_edge_shapes(H, L, causal, r_qk):
+    """Tiny and ragged sequences (one block of 8 queries; a last block of 8),
+    a single kept feature (r small enough that kk = 1), several heads."""
+    tag = f"edge H={H} L={L} causal={causal} r_qk={r_qk}"
+    log(tag)
+    q, k, v, Qd, Kd, Vd = make_qkv(H, L, seed=9)
+    idx, qs, Pt, pvs = run_producer(Qd, Kd, Vd, r_qk, causal)
+    idx_np = down(idx) if idx is not None else None
+    qs_np = down(qs) if qs is not None else None
+    Pt_np, pvs_np = down(Pt), down(pvs)
+    for h in range(H):
+        for g in range(-(-L // QB)):
+            check_block(q, k, v, idx_np, qs_np, Pt_np, pvs_np, h, g, L, r_qk, causal, True, tag)
