@@ -129,6 +129,7 @@ class Linear:
             return [("gemm", lambda: rmm.rmm_gemm(self.A, self.next_B(), None, kk, self.gr, Y=Y))], kk
         kpad = rmm.rmm_kk_pad(kk)
         idx = torch.empty((self.G, kpad), dtype=torch.int32, device=self.dev)
+        self.idx = idx
         Ap = torch.empty((self.M, kpad), dtype=torch.bfloat16, device=self.dev)
         ws = torch.empty(max(1, rmm.rmm_select_workspace_bytes(self.M, self.K, self.gr)), dtype=torch.uint8,
                          device=self.dev)
@@ -150,12 +151,26 @@ class Linear:
     def flops(self, r):
         return 2.0 * self.M * self.rmm.rmm_kk(r, self.K) * self.N
 
-    def gemm_bytes(self, r):
-        """Algorithmic HBM bytes of one reduced-GEMM launch: kept B rows (int8:
-        one byte per weight, plus the column scales), the A panel (or A), and Y."""
+    def kept_rows(self, r):
+        """B rows kept by at least one group (each is read from HBM at least
+        once): kk for one group, up to K for many; from the last selection run."""
         kk = self.rmm.rmm_kk(r, self.K)
+        cache = self.__dict__.setdefault("_rows", {})
+        if r not in cache:
+            if kk == self.K or self.G == 1 or getattr(self, "idx", None) is None or self.idx.shape[1] < kk:
+                cache[r] = kk
+            else:
+                cache[r] = int(self.torch.unique(self.idx[:, :kk]).numel())
+        return cache[r]
+
+    def gemm_bytes(self, r):
+        """Algorithmic HBM bytes of one reduced-GEMM launch: every B row some
+        group keeps, once (int8: one byte per weight, plus the column scales),
+        the A panel (or A), and Y."""
+        kk = self.rmm.rmm_kk(r, self.K)
+        rows = self.kept_rows(r)
         yb = 4 if self.f32 else 2
-        brow = (1.0 * kk * self.N + 4.0 * self.N) if self.q8 else 2.0 * kk * self.N
+        brow = (1.0 * rows * self.N + 4.0 * self.N) if self.q8 else 2.0 * rows * self.N
         return brow + 2.0 * self.M * kk + yb * self.M * self.N
 
     bound = property(lambda self: "hbm" if self.name in ("decode", "decode_q8") else "mfma")
