@@ -424,12 +424,23 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                 }
             }
             if (u - 1 >= T) {
-                // the P tile of step u-1: key sums (waves 4, 5), stores (waves 6, 7)
+                // the P tile of step u-1: with key scores, waves 4, 5 sum its key
+                // rows and waves 6, 7 store it; without, all four store it
                 const uint16_t *pb = pbuf[(u - 1) & 1];
                 const int64_t kp0 = (int64_t)(u - 1 - T) * kKT;
-                if (ht < 128) {
+                auto store_tile = [&](int first, int stride, int n) {
+                    for (int i = 0; i < n; ++i) {
+                        const int c = first + stride * i, r = c >> 4, qc = c & 15;
+                        const int64_t k = kp0 + r;
+                        if (k < Kvalid && 8 * qc < nq)
+                            *(u32x4 *)(Pt + (h * L + k) * L + q0 + 8 * qc) = *(const u32x4 *)&pb[r * kPitch + 8 * qc];
+                    }
+                };
+                if (!PVS) {
+                    store_tile(ht, 256, 8);
+                } else if (ht < 128) {
                     const int64_t k = kp0 + ht;
-                    if (PVS && k < Kvalid) {
+                    if (k < Kvalid) {
                         double mass = 0.0;
                         for (int c = 0; c < nq / 8; ++c) {
                             const u32x4 v = *(const u32x4 *)&pb[ht * kPitch + 8 * c];
@@ -442,13 +453,7 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                         pvs[(h * G + g) * L + k] = (float)(mass * vnorm[h * L + k]);
                     }
                 } else {
-#pragma unroll 4
-                    for (int i = 0; i < 16; ++i) {
-                        const int c = (ht - 128) + 128 * i, r = c >> 4, qc = c & 15;
-                        const int64_t k = kp0 + r;
-                        if (k < Kvalid && 8 * qc < nq)
-                            *(u32x4 *)(Pt + (h * L + k) * L + q0 + 8 * qc) = *(const u32x4 *)&pb[r * kPitch + 8 * qc];
-                    }
+                    store_tile(ht - 128, 128, 16);
                 }
             }
             if (u < U) __syncthreads();
