@@ -289,3 +289,50 @@ def test_edge_shapes(H, L, causal, r_qk):
     for h in range(H):
         for g in range(-(-L // QB)):
             check_block(q, k, v, idx_np, qs_np, Pt_np, pvs_np, h, g, L, r_qk, causal, True, tag)
+
+
+def test_graph_replay():
+    """The whole attention chain (feature select, producer with key scores,
+    key select, reduced P.V) captured in a HIP graph gives the eager result
+    on every replay, with eager work and synchronisations between replays."""
+    H, L, r = 2, 384, 0.5
+    q, k, v, Qd, Kd, Vd = make_qkv(H, L, seed=10)
+    G = L // QB
+    fidx = torch.zeros((H * G, rmm.rmm_kk_pad(D)), dtype=torch.int32, device=DEV)
+    qs = torch.zeros((H, G, D), dtype=torch.float32, device=DEV)
+    Pt = torch.zeros((H, L, L), dtype=torch.bfloat16, device=DEV)
+    pvs = torch.zeros((H, G, L), dtype=torch.float32, device=DEV)
+    kidx = torch.zeros((H * G, rmm.rmm_kk_pad(L)), dtype=torch.int32, device=DEV)
+    O_ = torch.zeros((H, L, D), dtype=torch.bfloat16, device=DEV)
+    wsp = torch.empty(max(1, int(rmm.lib().rmm_attn_probs_workspace_bytes(H, L, D, 1))), dtype=torch.uint8,
+                      device=DEV)
+
+    def step():
+        rmm.rmm_qk_select(Qd, Kd, r, QB, True, True, idx_out=fidx, scores_out=qs)
+        rmm.rmm_attn_probs(Qd, Kd, fidx, r, QB, True, Pt=Pt, V=Vd, pv_scores=pvs, ws=wsp)
+        rmm.rmm_pv_select_scores(pvs, r, QB, True, idx_out=kidx)
+        rmm.rmm_pv_gemm(Pt, Vd, r, kidx, QB, True, O=O_)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [down(x).copy() for x in (Pt, pvs, O_)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for x in (Pt, pvs, O_):
+            x.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [down(x) for x in (Pt, pvs, O_)]
+        for a, b, name in zip(got, ref, ("Pt", "pv scores", "O")):
+            assert np.array_equal(a, b), f"replay {rep}: {name} differs from the eager result"
+        rmm.rmm_pv_gemm(Pt, Vd, 1.0, None, QB, True)   # eager work between replays
+        torch.cuda.synchronize()
