@@ -139,13 +139,15 @@ class Linear:
             return [sel,
                     ("gather", lambda: rmm.rmm_gather(self.A, idx, kk, self.gr, Apanel=Ap, B=self.B, Bpanel=Bp)),
                     ("gemm", lambda: rmm.rmm_gemm(Ap, Bp, None, kk, self.gr, Y=Y))], kk
+        # bf16 activations: selection and gather in one call (one launch after
+        # the scores where the shape allows, else the two launches)
+        selg = ("select+gather", lambda: rmm.rmm_select_gather(self.A, r, self.gr, bnorm=self.bnorm, idx=idx,
+                                                                Apanel=Ap, ws=ws))
         if self.q8:
-            return [sel,
-                    ("gather", lambda: rmm.rmm_gather(self.A, idx, kk, self.gr, Apanel=Ap)),
+            return [selg,
                     ("gemm", lambda: rmm.rmm_gemm_q8(Ap, self.next_B(), self.scale, idx, kk, self.gr, Y=Y,
                                                      ws=wq))], kk
-        return [sel,
-                ("gather", lambda: rmm.rmm_gather(self.A, idx, kk, self.gr, Apanel=Ap)),
+        return [selg,
                 ("gemm", lambda: rmm.rmm_gemm(Ap, self.next_B(), idx, kk, self.gr, Y=Y))], kk
 
     def flops(self, r):

@@ -136,6 +136,23 @@ int rmm_gather(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const i
                const void *B, int64_t N, int64_t ldb, uint16_t *Bpanel, int64_t ldbp,
                void *stream);
 
+/* Selection and gather in one call: the same outputs as rmm_select followed
+ * by rmm_gather(A, dt, M, K, lda, idx, ldidx, rmm_kk(r, K), group_rows,
+ * Apanel, ldp, NULL, 0, 0, NULL, 0), bit for bit ("Estrategia de Selecao"
+ * then "Mecanismo Central").  For bf16 A with K <= 8192 and fewer than 512
+ * groups the gather runs inside the selection launch (each group's rows are
+ * split over several workgroups that stage them in LDS while the threshold is
+ * found), so the kept columns are formed without a second pass over idx;
+ * other shapes run the two launches.
+ *   arguments as rmm_select, plus
+ *   Apanel  [M][ldp] bf16, ldp >= rmm_kk_pad(rmm_kk(r, K)), device
+ *   ws      rmm_select_workspace_bytes(...) bytes (the same workspace)
+ * Errors: as rmm_select, and RMM_EINVAL for a bad Apanel or ldp. */
+int rmm_select_gather(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm,
+                      const void *B, int64_t N, int64_t ldb, double r, int64_t group_rows,
+                      int32_t *idx, int64_t ldidx, uint16_t *Apanel, int64_t ldp, float *scores,
+                      float *thresh, double *bound, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes rmm_gemm needs (currently 0 for every shape). */
 size_t rmm_gemm_workspace_bytes(int64_t M, int64_t N, int64_t kk, int64_t group_rows);
 

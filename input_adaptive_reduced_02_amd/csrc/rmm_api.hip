@@ -5,6 +5,7 @@
 // launches on the caller's stream.  No allocation, no host synchronisation.
 #include "../../include/rmm.h"
 #include "rmm_internal.h"
+#include "rmm_select.h"
 
 #include <cmath>
 
@@ -74,10 +75,17 @@ size_t rmm_select_workspace_bytes(int64_t M, int64_t K, int64_t group_rows, int 
     return n;
 }
 
-int rmm_select(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm,
-               const void *B, int64_t N, int64_t ldb, double r, int64_t group_rows, int32_t *idx,
-               int64_t ldidx, float *scores, float *thresh, double *bound, void *ws,
-               size_t ws_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Validation, B norms and column scores shared by rmm_select and
+// rmm_select_gather; on RMM_OK `sc` holds the G x K scores on the stream and
+// `sh` the selection shape.
+int linear_scores(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm, const void *B,
+                  int64_t N, int64_t ldb, double r, int64_t group_rows, int32_t *idx, int64_t ldidx,
+                  float *scores, float *thresh, double *bound, void *ws, size_t ws_bytes, hipStream_t s,
+                  float *&sc, SelectShape &sh)
 {
     if (M < 1 || K < 1 || group_rows < 1 || !ok_matrix(A, dt, K, lda)) return RMM_EINVAL;
     const int64_t kk = rmm_kk(r, K);
@@ -93,10 +101,9 @@ int rmm_select(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const d
     if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
     if (K > kSelectMaxK) return RMM_EUNSUPPORTED;
 
-    hipStream_t s = as_stream(stream);
     const int64_t G = (M + group_rows - 1) / group_rows;
     char *w = (char *)ws;
-    float *sc = scores;
+    sc = scores;
     if (!sc) {
         sc = (float *)w;
         w += align_up((size_t)G * K * sizeof(float));
@@ -108,13 +115,57 @@ int rmm_select(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const d
         bn = tmp;
     }
     if (hipError_t e = launch_colscore(A, dt, M, K, lda, bn, group_rows, sc, s)) return hip_status(e);
-    SelectShape sh{};
+    sh = SelectShape{};
     sh.groups = G;
     sh.K = K;
     sh.lds = K;
     sh.kk = kk;
     sh.pv = 0;
+    return RMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rmm_select(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm,
+               const void *B, int64_t N, int64_t ldb, double r, int64_t group_rows, int32_t *idx,
+               int64_t ldidx, float *scores, float *thresh, double *bound, void *ws,
+               size_t ws_bytes, void *stream)
+{
+    hipStream_t s = as_stream(stream);
+    float *sc = nullptr;
+    SelectShape sh;
+    if (int st = linear_scores(A, dt, M, K, lda, bnorm, B, N, ldb, r, group_rows, idx, ldidx, scores, thresh,
+                               bound, ws, ws_bytes, s, sc, sh))
+        return st;
     return hip_status(launch_select(sc, sh, idx, ldidx, thresh, bound, s));
+}
+
+int rmm_select_gather(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm,
+                      const void *B, int64_t N, int64_t ldb, double r, int64_t group_rows, int32_t *idx,
+                      int64_t ldidx, uint16_t *Apanel, int64_t ldp, float *scores, float *thresh,
+                      double *bound, void *ws, size_t ws_bytes, void *stream)
+{
+    const int64_t kk = rmm_kk(r, K);
+    if (kk < 1 || !ok_matrix(Apanel, RMM_BF16, pad_up(kk), ldp)) return RMM_EINVAL;
+    hipStream_t s = as_stream(stream);
+    float *sc = nullptr;
+    SelectShape sh;
+    if (int st = linear_scores(A, dt, M, K, lda, bnorm, B, N, ldb, r, group_rows, idx, ldidx, scores, thresh,
+                               bound, ws, ws_bytes, s, sc, sh))
+        return st;
+    SelectGather ga{};
+    int nrb = 0;
+    if (select_gather_plan(dt, M, K, lda, group_rows, ga, nrb)) {
+        ga.A = (const uint16_t *)A;
+        ga.Ap = Apanel;
+        ga.ldp = ldp;
+        return hip_status(launch_select_gather(sc, sh, idx, ldidx, thresh, bound, ga, nrb, s));
+    }
+    if (hipError_t e = launch_select(sc, sh, idx, ldidx, thresh, bound, s)) return hip_status(e);
+    return hip_status(launch_gather(A, dt, M, K, lda, idx, ldidx, kk, group_rows, Apanel, ldp, nullptr, 0, 0,
+                                    nullptr, 0, s));
 }
 
 int rmm_gather(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const int32_t *idx,

@@ -30,7 +30,18 @@
 // exchange; keys == T are kept in index order until kk.  No atomics decide an
 // order and no floating-point sum decides anything, so the output is
 // deterministic.
+//
+// Select + gather in one launch (NRB > 0): the group's rows are split over
+// `slices` workgroups, each of which runs the whole selection of its group
+// (identical, deterministic work) while its own rows of A stream into LDS
+// with DMA loads (issued after the histogram, in flight during the rest of
+// the selection).  After the threshold and the ordered compaction (kept
+// indices into an LDS list) every workgroup picks its rows' kept elements out
+// of LDS into the bf16 panel, 8 per lane and one 16-byte store; the first
+// slice also writes the index row, threshold and bound.  The panel equals the
+// one the separate gather writes from the same index row.
 #include "rmm_internal.h"
+#include "rmm_select.h"
 
 namespace rmm {
 
@@ -95,13 +106,28 @@ __device__ __forceinline__ uint64_t count3(const int32_t *cand, uint32_t first, 
     return (uint64_t)m1 | ((uint64_t)m2 << 21) | ((uint64_t)m3 << 42);
 }
 
-template <int KPT>
+// NRB = 0: selection only, one workgroup per group.  NRB > 0: selection and
+// gather, `ga.slices` workgroups per group, each staging at most NRB 1 KiB
+// blocks of rows per wave (16 * NRB KiB per workgroup).
+// DMA: every lane copies 16 bytes from its global address to LDS[lds + 16*lane]
+// (global_load_lds_dwordx4; no register result, so nothing waits for it until
+// an explicit s_waitcnt).
+__device__ __forceinline__ void sel_dma16(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t sel_lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+template <int KPT, int NRB>
 __global__ void __launch_bounds__(kSelectThreads)
 k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__ idx, int64_t ldidx,
-         float *__restrict__ thresh, double *__restrict__ bound)
+         float *__restrict__ thresh, double *__restrict__ bound, SelectGather ga)
 {
     __shared__ uint32_t hist[kBuckets];
-    __shared__ int32_t cand[KPT * kSelectThreads];
+    __shared__ __attribute__((aligned(16))) int32_t cand[KPT * kSelectThreads];   // later the kept list
+    __shared__ __attribute__((aligned(1024))) unsigned char stage[NRB > 0 ? NRB * 16 * 1024 : 16];
     __shared__ uint64_t red[2][kNW];
     __shared__ uint64_t wsum64[kNW];
     __shared__ uint32_t wtot[2][kNW];
@@ -110,7 +136,9 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     __shared__ int32_t s_last, s_bin, s_T;
     __shared__ int64_t s_above;
 
-    const int64_t grp = blockIdx.x;
+    const int64_t grp = NRB > 0 ? blockIdx.x / ga.slices : blockIdx.x;
+    const int slice = NRB > 0 ? (int)(blockIdx.x % ga.slices) : 0;
+    const bool lead = slice == 0;   // the workgroup that writes idx, thresh and bound
     int64_t K, kk;
     if (sh.pv) {
         const int64_t g = grp % sh.Gq;
@@ -195,6 +223,31 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     __syncthreads();
     const int bin = s_bin;
     const int64_t need = kk - s_above;   // how many of the bucket's keys are kept (>= 1)
+    // The slice's rows of A into LDS, in flight during the rest of the
+    // selection: no compiler-placed wait below is for these loads (the keys
+    // have arrived, and the barriers wait for LDS operations only); an
+    // explicit wait precedes the pick.  Row i of the slice goes to LDS byte
+    // i * lda * 2: the rows are one contiguous global range, copied in 1 KiB
+    // blocks (block b by wave b % 16), and lanes past its end re-read its
+    // start into block space no row uses.
+    int64_t srow0 = 0, sbytes = 0;
+    int nrows = 0;
+    if constexpr (NRB > 0) {
+        const int64_t g0 = grp * ga.gr;
+        const int64_t gend = (g0 + ga.gr < ga.M) ? g0 + ga.gr : ga.M;
+        srow0 = g0 + (int64_t)slice * ga.rows;
+        nrows = (int)((gend - srow0 < ga.rows) ? (gend - srow0 > 0 ? gend - srow0 : 0) : ga.rows);
+        sbytes = (int64_t)nrows * ga.lda * 2;
+        const char *src = (const char *)ga.A + srow0 * ga.lda * 2;
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        const uint32_t st0 = sel_lds_addr(stage);
+#pragma unroll
+        for (int i = 0; i < NRB; ++i) {
+            const int b = wv + kNW * i;
+            const int64_t o = (int64_t)b * 1024 + 16 * lane;
+            if ((int64_t)b * 1024 < sbytes) sel_dma16(o < sbytes ? src + o : src, st0 + b * 1024);
+        }
+    }
 
     // ---- 2. the bucket's keys to LDS, then T among them
     uint32_t nc = 0;
@@ -323,26 +376,65 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
             ++eq_seen;
         }
         if (keep) {
-            if (pos < kk) out[pos] = k;   // always true when T is the kk-th key
+            if (pos < kk) {   // always true when T is the kk-th key
+                if constexpr (NRB > 0) cand[pos] = k;   // every reader of cand passed a barrier since
+                else out[pos] = k;
+            }
             if (pos == kk - 1) s_last = k;
             ++pos;
         } else {
             dropped += (double)__int_as_float(key[i]);
         }
     }
-    if (tid == 0 && thresh) thresh[grp] = __int_as_float(T);
+    if (lead && tid == 0 && thresh) thresh[grp] = __int_as_float(T);
     if (bound) {
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) dropped += __shfl_xor(dropped, m, 64);
         if (lane == 0) fsum[wave] = dropped;
     }
+    if constexpr (NRB > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's row blocks
     __syncthreads();
     const int64_t padded = pad_up(kk);
-    for (int64_t j = kk + tid; j < padded; j += kSelectThreads) out[j] = s_last;
-    if (bound && tid == 0) {
-        double b = 0.0;
-        for (int w = 0; w < kNW; ++w) b += fsum[w];
-        bound[grp] = b;
+    if (lead) {
+        if constexpr (NRB > 0)
+            for (int64_t j = tid; j < kk; j += kSelectThreads) out[j] = cand[j];
+        for (int64_t j = kk + tid; j < padded; j += kSelectThreads) out[j] = s_last;
+        if (bound && tid == 0) {
+            double b = 0.0;
+            for (int w = 0; w < kNW; ++w) b += fsum[w];
+            bound[grp] = b;
+        }
+    }
+    if constexpr (NRB > 0) {
+        // the rows and the kept list are in LDS: panel chunk c of row i holds
+        // the row's elements at kept indices 8c .. 8c+7 (zero past kk).
+        // (row, chunk) items in row-major order, thread tid takes items tid,
+        // tid + 1024, ..., stepped without division
+        const int cpr = (int)(padded / 8);
+        const int kk32 = (int)kk;
+        const int di = kSelectThreads / cpr, dc = kSelectThreads % cpr;
+        int i = tid / cpr, c = tid % cpr;
+        for (; i < nrows; i += di, c += dc) {
+            if (c >= cpr) {
+                c -= cpr;
+                if (++i >= nrows) break;
+            }
+            const int j0 = 8 * c;
+            const uint16_t *row = (const uint16_t *)(stage + (size_t)i * (size_t)ga.lda * 2);
+            uint32_t h[8];
+            if (j0 + 8 <= kk32) {
+                const int4 i0 = *(const int4 *)(cand + j0);
+                const int4 i1 = *(const int4 *)(cand + j0 + 4);
+                const int32_t ks[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+                for (int q = 0; q < 8; ++q) h[q] = row[ks[q]];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) h[q] = (j0 + q < kk32) ? row[cand[j0 + q]] : 0u;
+            }
+            *(uint4 *)(ga.Ap + (srow0 + i) * ga.ldp + j0) =
+                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        }
     }
 }
 
@@ -573,7 +665,7 @@ hipError_t launch_select(const float *scores, const SelectShape &sh, int32_t *id
     }
     const int64_t kpt = (sh.K + kSelectThreads - 1) / kSelectThreads;
 #define RMM_SELECT_LAUNCH(N) \
-    hipLaunchKernelGGL(k_select<N>, grid, block, 0, s, scores, sh, idx, ldidx, thresh, bound)
+    hipLaunchKernelGGL((k_select<N, 0>), grid, block, 0, s, scores, sh, idx, ldidx, thresh, bound, SelectGather{})
     if (kpt <= 1) RMM_SELECT_LAUNCH(1);
     else if (kpt <= 2) RMM_SELECT_LAUNCH(2);
     else if (kpt <= 4) RMM_SELECT_LAUNCH(4);
@@ -581,6 +673,57 @@ hipError_t launch_select(const float *scores, const SelectShape &sh, int32_t *id
     else if (kpt <= 16) RMM_SELECT_LAUNCH(16);
     else RMM_SELECT_LAUNCH(32);
 #undef RMM_SELECT_LAUNCH
+    return hipGetLastError();
+}
+
+bool select_gather_plan(int dt, int64_t M, int64_t K, int64_t lda, int64_t group_rows, SelectGather &ga,
+                        int &nrb)
+{
+    const int64_t G = (M + group_rows - 1) / group_rows;
+    const int64_t kpt = (K + kSelectThreads - 1) / kSelectThreads;
+    if (dt != 1 || kpt > 8 || G >= 512) return false;
+    const int64_t rows = group_rows < M ? group_rows : M;   // rows of the largest group
+    const int64_t row_bytes = lda * 2;
+    const int64_t cap = 6 * 16 * 1024;                      // largest staging (NRB = 6)
+    if (row_bytes > cap) return false;
+    // about 256 workgroups in all, fewer rows per slice if they do not fit
+    int64_t slices = 256 / G;
+    if (slices < 1) slices = 1;
+    if (slices > rows) slices = rows;
+    int64_t per = (rows + slices - 1) / slices;
+    if (per * row_bytes > cap) per = cap / row_bytes;
+    slices = (rows + per - 1) / per;
+    if (G * slices > 512) return false;
+    const int64_t bytes = per * row_bytes;
+    nrb = bytes <= 16384 ? 1 : bytes <= 32768 ? 2 : bytes <= 65536 ? 4 : 6;
+    ga.M = M;
+    ga.lda = lda;
+    ga.gr = group_rows;
+    ga.slices = (int)slices;
+    ga.rows = per;
+    return true;
+}
+
+hipError_t launch_select_gather(const float *scores, const SelectShape &sh, int32_t *idx, int64_t ldidx,
+                                float *thresh, double *bound, const SelectGather &ga, int nrb, hipStream_t s)
+{
+    dim3 grid((unsigned)(sh.groups * ga.slices)), block(kSelectThreads);
+    const int64_t kpt = (sh.K + kSelectThreads - 1) / kSelectThreads;
+#define RMM_SG_LAUNCH(N, R) \
+    hipLaunchKernelGGL((k_select<N, R>), grid, block, 0, s, scores, sh, idx, ldidx, thresh, bound, ga)
+#define RMM_SG_NRB(N)                        \
+    do {                                     \
+        if (nrb == 1) RMM_SG_LAUNCH(N, 1);   \
+        else if (nrb == 2) RMM_SG_LAUNCH(N, 2); \
+        else if (nrb == 4) RMM_SG_LAUNCH(N, 4); \
+        else RMM_SG_LAUNCH(N, 6);            \
+    } while (0)
+    if (kpt <= 1) RMM_SG_NRB(1);
+    else if (kpt <= 2) RMM_SG_NRB(2);
+    else if (kpt <= 4) RMM_SG_NRB(4);
+    else RMM_SG_NRB(8);
+#undef RMM_SG_NRB
+#undef RMM_SG_LAUNCH
     return hipGetLastError();
 }
 

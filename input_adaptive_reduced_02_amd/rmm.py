@@ -62,6 +62,9 @@ def _declare(L):
     L.rmm_select.restype = _I
     L.rmm_select.argtypes = [_P, _I, _L, _L, _L, _P, _P, _L, _L, _Dbl, _L, _P, _L, _P, _P, _P, _P, _S, _P]
     L.rmm_gather.restype = _I
+    L.rmm_select_gather.restype = _I
+    L.rmm_select_gather.argtypes = [_P, _I, _L, _L, _L, _P, _P, _L, _L, _Dbl, _L, _P, _L, _P, _L, _P, _P, _P,
+                                    _P, _S, _P]
     L.rmm_gather.argtypes = [_P, _I, _L, _L, _L, _P, _L, _L, _L, _P, _L, _P, _L, _L, _P, _L, _P]
     L.rmm_gemm_workspace_bytes.restype = _S
     L.rmm_gemm_workspace_bytes.argtypes = [_L, _L, _L, _L]
@@ -180,6 +183,31 @@ def rmm_select(A, r, group_rows, bnorm=None, B=None, idx=None, scores=None, thre
         group_rows, _ptr(idx), _ld(idx), _ptr(scores), _ptr(thresh), _ptr(bound), _ptr(w), need,
         _stream(A)))
     return idx
+
+
+def rmm_select_gather(A, r, group_rows, bnorm=None, B=None, idx=None, Apanel=None, scores=None, thresh=None,
+                      bound=None, ws=None):
+    """rmm_select and rmm_gather of its indices in one call: (idx [G, kk_pad]
+    int32, bf16 panel [M, kk_pad])."""
+    M, K = A.shape
+    kk = rmm_kk(r, K)
+    if kk < 1:
+        raise ValueError("r must lie in (0, 1]")
+    G = -(-M // group_rows)
+    kpad = rmm_kk_pad(kk)
+    if idx is None:
+        idx = torch.empty((G, kpad), dtype=torch.int32, device=A.device)
+    if Apanel is None:
+        Apanel = torch.empty((M, kpad), dtype=torch.bfloat16, device=A.device)
+    from_B = bnorm is None and B is not None
+    need = rmm_select_workspace_bytes(M, K, group_rows, scores is not None, from_B)
+    w = _ws(need, A.device, ws)
+    N, ldb = (B.shape[1], _ld(B)) if from_B else (0, 0)
+    _check("rmm_select_gather", lib().rmm_select_gather(
+        _ptr(A), _dt(A), M, K, _ld(A), _ptr(bnorm), _ptr(B) if from_B else None, N, ldb, float(r),
+        group_rows, _ptr(idx), _ld(idx), _ptr(Apanel), _ld(Apanel), _ptr(scores), _ptr(thresh), _ptr(bound),
+        _ptr(w), need, _stream(A)))
+    return idx, Apanel
 
 
 def rmm_gather(A, idx, kk, group_rows, Apanel=None, B=None, Bpanel=None):
@@ -359,8 +387,7 @@ def linear_q8(A, Bq, scale, r, group_rows, bnorm, ydt=torch.bfloat16):
     kk = rmm_kk(r, K)
     if kk == K:
         return rmm_gemm_q8(A, Bq, scale, None, K, group_rows, ydt=ydt)
-    idx = rmm_select(A, r, group_rows, bnorm=bnorm)
-    Ap, _ = rmm_gather(A, idx, kk, group_rows)
+    idx, Ap = rmm_select_gather(A, r, group_rows, bnorm=bnorm)
     return rmm_gemm_q8(Ap, Bq, scale, idx, kk, group_rows, ydt=ydt)
 
 
@@ -376,15 +403,12 @@ def linear(A, B, r, group_rows, bnorm=None, ydt=torch.bfloat16, activation_only=
     kk = rmm_kk(r, K)
     if kk == K and A.dtype == torch.bfloat16 and B.dtype == torch.bfloat16 and K % 8 == 0:
         return rmm_gemm(A, B, None, K, group_rows, ydt=ydt)
-    if activation_only:
-        idx = rmm_select(A, r, group_rows)
-    else:
-        idx = rmm_select(A, r, group_rows, bnorm=bnorm, B=B if bnorm is None else None)
-    G = idx.shape[0]
+    sel_B = None if activation_only or bnorm is not None else B
     if B.dtype != torch.bfloat16:
-        if G != 1:
+        idx = rmm_select(A, r, group_rows, bnorm=bnorm, B=sel_B)
+        if idx.shape[0] != 1:
             raise ValueError("binary32 B needs a single selection group (packed B panel)")
         Ap, Bp = rmm_gather(A, idx, kk, group_rows, B=B)
         return rmm_gemm(Ap, Bp, None, kk, group_rows, ydt=ydt)
-    Ap, _ = rmm_gather(A, idx, kk, group_rows)
+    idx, Ap = rmm_select_gather(A, r, group_rows, bnorm=bnorm, B=sel_B)
     return rmm_gemm(Ap, B, idx, kk, group_rows, ydt=ydt)

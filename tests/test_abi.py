@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -135,6 +135,24 @@ def test_validation_rejects_bad_arguments():
     assert sel(bn=ctypes.c_void_p((1 << 20) + 4)) == EINVAL
     assert sel(bn=None, B=P, N=8, ldb=4) == EINVAL
     assert sel(K=40000, lda=40000, ldidx=20032, wsb=4 * 40000 * 4) == EUNSUP
+
+    # select_gather: the select arguments plus (Ap, ldp) after ldidx
+    def selg(Ap=P2, ldp=64, **kw):
+        a = dict(good, **kw)
+        return L.rmm_select_gather(a["A"], a["dt"], a["M"], a["K"], a["lda"], a["bn"], a["B"], a["N"],
+                                   a["ldb"], a["r"], a["gr"], a["idx"], a["ldidx"], Ap, ldp, a["sc"], a["th"],
+                                   a["bd"], a["ws"], a["wsb"], None)
+    for bad_r in (0.0, 1.5, nan):
+        assert selg(r=bad_r) == EINVAL, bad_r
+    assert selg(Ap=None) == EINVAL
+    assert selg(Ap=MIS) == EINVAL
+    assert selg(ldp=32) == EINVAL             # < kk_pad
+    assert selg(ldp=68) == EINVAL             # rows not 16-byte aligned
+    assert selg(M=0) == EINVAL
+    assert selg(A=None) == EINVAL
+    assert selg(ldidx=32) == EINVAL
+    assert selg(wsb=ws_need - 1) == EINVAL
+    assert selg(K=40000, lda=40000, ldidx=20032, ldp=20032, wsb=4 * 40000 * 4) == EUNSUP
     # gather(A, dt, M, K, lda, idx, ldidx, kk, gr, Ap, ldp, B, N, ldb, Bp, ldbp, stream)
     assert L.rmm_gather(P, BF, 64, 64, 64, P2, 64, 0, 64, P3, 64, None, 0, 0, None, 0, None) == EINVAL
     assert L.rmm_gather(P, BF, 64, 64, 64, P2, 64, 65, 64, P3, 128, None, 0, 0, None, 0, None) == EINVAL

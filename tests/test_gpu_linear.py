@@ -40,13 +40,16 @@ def run_chain(c, r, gr, bnorm):
     thresh = torch.empty(G, dtype=torch.float32, device=DEV)
     bound = torch.empty(G, dtype=torch.float64, device=DEV)
     idx = torch.zeros((G, rmm.rmm_kk_pad(kk)), dtype=torch.int32, device=DEV)
-    rmm.rmm_select(A, r, gr, bnorm=bnorm, idx=idx, scores=scores, thresh=thresh, bound=bound)
-    check_index_range(idx, K)
     if c["f32"]:
+        rmm.rmm_select(A, r, gr, bnorm=bnorm, idx=idx, scores=scores, thresh=thresh, bound=bound)
+        check_index_range(idx, K)
         Ap, Bp = rmm.rmm_gather(A, idx, kk, gr, B=B)
         Y = rmm.rmm_gemm(Ap, Bp, None, kk, gr, ydt=torch.float32)
     else:
-        Ap, _ = rmm.rmm_gather(A, idx, kk, gr)
+        # the launch sequence the benchmark times: select + gather in one call
+        _, Ap = rmm.rmm_select_gather(A, r, gr, bnorm=bnorm, idx=idx, scores=scores, thresh=thresh,
+                                      bound=bound)
+        check_index_range(idx, K)
         Y = rmm.rmm_gemm(Ap, B, idx, kk, gr)
     torch.cuda.synchronize()
     return idx, scores, thresh, bound, Ap, Y
@@ -294,3 +297,74 @@ def test_full_size_activation_only(workload, r):
     Yref = np.stack([O.reduced(c["A64"], c["B64"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
     Sabs = np.stack([O.reduced(c["A64abs"], c["B64abs"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
     check_output(widen(Y)[rows], Yref, Sabs, kk, tag + f" ({len(rows)} rows)")
+
+
+# ---------------------------------------------------------------- select + gather in one call
+SG = [
+    # (workload, M, K, N, group_rows, r, lda): the fused kernel's slicing and
+    # staging sizes, ragged groups, a padded leading dimension, and shapes that
+    # take the two-launch fallback (K > 8192, 512 or more groups)
+    ("attn_proj", 2048, 4096, 8, 128, 0.5, 4096),   # 16 groups x 16 slices of 8 rows (64 KiB staged)
+    ("attn_proj", 2048, 4096, 8, 128, 0.3, 4096),
+    ("decode", 64, 8192, 8, 64, 0.3, 8192),         # one group, 64 slices of one 16 KiB row
+    ("attn_proj", 300, 1000, 8, 128, 0.37, 1000),   # groups 128, 128, 44; rows of 2000 bytes
+    ("attn_proj", 384, 8192, 8, 128, 0.5, 8200),    # 3 groups: 2 rows per slice, lda > K
+    ("attn_proj", 100, 2050, 8, 16, 0.9, 2056),     # 7 groups, ragged last group, kk not a multiple of 8
+    ("mlp_down", 200, 136, 8, 32, 0.25, 136),       # short rows, one row per slice
+    ("attn_proj", 2048, 5120, 8, 128, 0.5, 5120),   # 80 KiB staged per workgroup (the largest staging)
+    ("mlp_down", 512, 1500, 8, 64, 0.6, 1504),      # 2 keys per thread, lda > K
+    ("mlp_down", 256, 14336, 8, 128, 0.5, 14336),   # K > 8192: two launches
+    ("attn_proj", 4096, 1000, 8, 8, 0.3, 1000),     # 512 groups: two launches
+]
+
+
+@pytest.mark.parametrize("case", SG, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-g{c[4]}-r{c[5]}-ld{c[6]}")
+def test_select_gather_equals_select_then_gather(case):
+    """rmm_select_gather returns, bit for bit, what rmm_select followed by
+    rmm_gather returns (indices with padding, scores, thresholds, bounds,
+    panel); the kept sets and the panel are also checked against the oracle.
+    Each case runs twice, the second time on a smaller input that reuses the
+    output buffers, to catch state left over from a previous call."""
+    workload, M, K, N, gr, r, lda = case
+    tag = f"select+gather {workload} {M}x{K} gr={gr} r={r} lda={lda}"
+    log(f"case {tag}")
+    c = make_case(workload, M, K, N, seed=21)
+    if lda > K:
+        wide = torch.zeros((M, lda), dtype=c["A"].dtype, device=DEV)
+        wide[:, :K] = c["A"]
+        c["A"] = wide[:, :K]
+    kk = rmm.rmm_kk(r, K)
+    kpad = rmm.rmm_kk_pad(kk)
+    bnorm = rmm.rmm_rownorms(c["B"])
+    for MM in (M, max(1, M // 3 + 5)):
+        A = c["A"][:MM]
+        G = -(-MM // gr)
+        outs = []
+        for fused in (False, True):
+            sc = torch.full((G, K), -1.0, dtype=torch.float32, device=DEV)
+            th = torch.full((G,), -1.0, dtype=torch.float32, device=DEV)
+            bd = torch.full((G,), -1.0, dtype=torch.float64, device=DEV)
+            ix = torch.full((G, kpad), -7, dtype=torch.int32, device=DEV)
+            ap = torch.full((MM, kpad), 3.0, dtype=torch.bfloat16, device=DEV)
+            if fused:
+                rmm.rmm_select_gather(A, r, gr, bnorm=bnorm, idx=ix, Apanel=ap, scores=sc, thresh=th, bound=bd)
+            else:
+                rmm.rmm_select(A, r, gr, bnorm=bnorm, idx=ix, scores=sc, thresh=th, bound=bd)
+                check_index_range(ix, K)
+                rmm.rmm_gather(A, ix, kk, gr, Apanel=ap)
+            torch.cuda.synchronize()
+            outs.append((ix, sc, th, bd, ap))
+        for name, a, b in zip(("idx", "scores", "thresh", "bound", "panel"), *outs):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), f"{tag} M={MM}: {name}"
+        # the kept sets and the panel against the oracle
+        A64 = c["A64"][:MM]
+        sel = O.select(A64, r, gr, O.rownorms(c["B64"]))
+        ig = down(outs[1][0])
+        for g in range(G):
+            compare_sets(ig[g], sel, g, kk, tag)
+        pan = down(outs[1][4])
+        A_bits = c["raw"]["A"]
+        for m in np.unique(np.linspace(0, MM - 1, 17).astype(int)):
+            assert np.array_equal(pan[m, :kk], A_bits[m, ig[m // gr, :kk]]), f"{tag}: panel row {m}"
+            assert np.all(pan[m, kk:] == 0), f"{tag}: panel padding row {m}"
