@@ -19,12 +19,14 @@
 //      outlier channels do not crowd the bulk of the scores into a few
 //      buckets; the LDS atomics rarely collide and the threshold's bucket
 //      holds few keys.
-//   2. The bucket's keys are copied to LDS and T is found among them bit by
-//      bit, two bits per round (three candidate prefixes counted with
-//      wavefront ballots).  Up to 1024 candidates one wave does this alone,
-//      with the candidates in registers and no barriers, starting below the
-//      high bits its smallest and largest candidate share (T lies between
-//      them); beyond that all 16 waves share the search through LDS.
+//   2. The bucket's keys are copied to LDS (in any order, places reserved by
+//      one LDS atomic per wave and key slot) and T is found among them: up to
+//      64 candidates by exact rank, up to 1024 bit by bit, two bits per round
+//      (three candidate prefixes counted with wavefront ballots) starting
+//      below the high bits the smallest and largest candidate share (T lies
+//      between them).  Every wave does this on its own, with the candidates
+//      in registers, so no barrier broadcasts T; beyond 1024 candidates all
+//      16 waves share the search through LDS.
 // Then the ordered compaction: per-wave exclusive counts of keys > T and == T
 // come from ballots masked to the lower lanes, per-wave totals from one LDS
 // exchange; keys == T are kept in index order until kk.  No atomics decide an
@@ -130,10 +132,11 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     __shared__ __attribute__((aligned(1024))) unsigned char stage[NRB > 0 ? NRB * 16 * 1024 : 16];
     __shared__ uint64_t red[2][kNW];
     __shared__ uint64_t wsum64[kNW];
-    __shared__ uint32_t wtot[2][kNW];
+    __shared__ uint32_t wtot[kNW];
     __shared__ int32_t imin[kNW], imax[kNW];
     __shared__ double fsum[kNW];
-    __shared__ int32_t s_last, s_bin, s_T;
+    __shared__ int32_t s_last, s_bin;
+    __shared__ uint32_t s_nc;
     __shared__ int64_t s_above;
 
     const int64_t grp = NRB > 0 ? blockIdx.x / ga.slices : blockIdx.x;
@@ -154,7 +157,10 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     const int64_t base = (int64_t)tid * kpt;
 
     for (int i = tid; i < kBuckets; i += kSelectThreads) hist[i] = 0;
-    if (tid == 0) s_last = 0;   // written again (by the kk-th keeper) after several barriers
+    if (tid == 0) {
+        s_last = 0;   // written again (by the kk-th keeper) after several barriers
+        s_nc = 0;     // candidate count, first added to after two barriers
+    }
     int32_t key[KPT];           // -1 marks "no key here"; real keys are >= 0
     int32_t lo = 0x7fffffff, hi = 0;
     if (KPT % 4 == 0 && kpt == KPT && base + KPT <= K && ((uintptr_t)(s + base) & 15u) == 0) {
@@ -210,7 +216,7 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         // thread t owns buckets 2t, 2t+1
         const uint32_t hlo = hist[2 * tid], hhi = hist[2 * tid + 1];
         uint32_t total;
-        const uint32_t incl = block_excl_scan(hlo + hhi, wtot[0], total) + hlo + hhi;
+        const uint32_t incl = block_excl_scan(hlo + hhi, wtot, total) + hlo + hhi;
         const int64_t above = (int64_t)total - incl;   // keys in buckets above 2t+1
         if (above < kk && kk <= above + hhi) {
             s_bin = 2 * tid + 1;
@@ -249,82 +255,80 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         }
     }
 
-    // ---- 2. the bucket's keys to LDS, then T among them
-    uint32_t nc = 0;
+    // ---- 2. the bucket's keys to LDS, in any order (T depends on their
+    // values only): per key slot one wave-aggregated LDS atomic reserves the
+    // wave's places.  Then every wave finds T on its own (no broadcast
+    // barrier), unless there are more than 1024 candidates.
+    const uint64_t below = lanes_below(lane);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) nc += (key[i] >= 0 && bucket(key[i]) == bin);
-    uint32_t n1;
-    uint32_t pos_c = block_excl_scan(nc, wtot[1], n1);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-        if (key[i] >= 0 && bucket(key[i]) == bin) cand[pos_c++] = key[i];
+    for (int i = 0; i < KPT; ++i) {
+        const bool in = key[i] >= 0 && bucket(key[i]) == bin;
+        const uint64_t m = __ballot(in);
+        if (m) {
+            uint32_t at = 0;
+            if (lane == 0) at = atomicAdd(&s_nc, (uint32_t)__popcll(m));
+            at = __shfl(at, 0, 64);
+            if (in) cand[at + __popcll(m & below)] = key[i];
+        }
+    }
     __syncthreads();
+    const uint32_t n1 = s_nc;
     int32_t T = 0;
     if (n1 <= 64) {
-        // few candidates: lane i of wave 0 takes candidate i and counts the
-        // larger and the equal ones; T is a candidate with #(> T) < need <= #(>= T)
-        if (wave == 0) {
-            const int32_t mine = lane < (int)n1 ? cand[lane] : -1;
-            uint32_t gt = 0, ge = 0;
-            for (uint32_t i = 0; i < n1; ++i) {
-                const int32_t x = cand[i];
-                gt += x > mine;
-                ge += x >= mine;
-            }
-            const uint64_t hit = __ballot(lane < (int)n1 && gt < need && need <= ge);
-            const int32_t t = __shfl(mine, __builtin_ctzll(hit), 64);   // whole wave active
-            if (lane == 0) s_T = t;
+        // few candidates: lane i takes candidate i and counts the larger and
+        // the equal ones; T is a candidate with #(> T) < need <= #(>= T)
+        const int32_t mine = lane < (int)n1 ? cand[lane] : -1;
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t i = 0; i < n1; ++i) {
+            const int32_t x = cand[i];
+            gt += x > mine;
+            ge += x >= mine;
         }
-        __syncthreads();
-        T = s_T;
+        const uint64_t hit = __ballot(lane < (int)n1 && gt < need && need <= ge);
+        T = __shfl(mine, __builtin_ctzll(hit), 64);   // whole wave active
     } else if (n1 <= 1024) {
-        // one wave, candidates held in registers (16 slots of 64)
-        if (wave == 0) {
-            int32_t c[16];
-            int32_t lo = 0x7fffffff, hi = 0;
+        // candidates held in registers (16 slots of 64)
+        int32_t c[16];
+        int32_t lo = 0x7fffffff, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t i = j * 64 + lane;
+            c[j] = (i < n1) ? cand[i] : -1;
+            if (c[j] >= 0) {
+                lo = min(lo, c[j]);
+                hi = max(hi, c[j]);
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            lo = min(lo, __shfl_xor(lo, m, 64));
+            hi = max(hi, __shfl_xor(hi, m, 64));
+        }
+        // lo <= T <= hi, so T shares their common high bits; search the rest
+        const int hb = (lo == hi) ? -1 : 31 - __clz(lo ^ hi);
+        T = (hb < 0) ? lo : (lo & ~((int32_t)((2u << hb) - 1u)));
+        const int nslots = (int)((n1 + 63) / 64);
+        int b = hb;
+        for (; b >= 1; b -= 2) {
+            const int32_t c1 = T | (1 << (b - 1)), c2 = T | (2 << (b - 1)), c3 = T | (3 << (b - 1));
+            uint32_t m1 = 0, m2 = 0, m3 = 0;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const uint32_t i = j * 64 + lane;
-                c[j] = (i < n1) ? cand[i] : -1;
-                if (c[j] >= 0) {
-                    lo = min(lo, c[j]);
-                    hi = max(hi, c[j]);
+                if (j < nslots) {
+                    m1 += __popcll(__ballot(c[j] >= c1));
+                    m2 += __popcll(__ballot(c[j] >= c2));
+                    m3 += __popcll(__ballot(c[j] >= c3));
                 }
             }
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) {
-                lo = min(lo, __shfl_xor(lo, m, 64));
-                hi = max(hi, __shfl_xor(hi, m, 64));
-            }
-            // lo <= T <= hi, so T shares their common high bits; search the rest
-            const int hb = (lo == hi) ? -1 : 31 - __clz(lo ^ hi);
-            T = (hb < 0) ? lo : (lo & ~((int32_t)((2u << hb) - 1u)));
-            const int nslots = (int)((n1 + 63) / 64);
-            int b = hb;
-            for (; b >= 1; b -= 2) {
-                const int32_t c1 = T | (1 << (b - 1)), c2 = T | (2 << (b - 1)), c3 = T | (3 << (b - 1));
-                uint32_t m1 = 0, m2 = 0, m3 = 0;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    if (j < nslots) {
-                        m1 += __popcll(__ballot(c[j] >= c1));
-                        m2 += __popcll(__ballot(c[j] >= c2));
-                        m3 += __popcll(__ballot(c[j] >= c3));
-                    }
-                }
-                T |= ((m3 >= need) ? 3 : (m2 >= need) ? 2 : (m1 >= need) ? 1 : 0) << (b - 1);
-            }
-            if (b == 0) {
-                uint32_t m1 = 0;
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    if (j < nslots) m1 += __popcll(__ballot(c[j] >= (T | 1)));
-                if (m1 >= need) T |= 1;
-            }
-            if (lane == 0) s_T = T;
+            T |= ((m3 >= need) ? 3 : (m2 >= need) ? 2 : (m1 >= need) ? 1 : 0) << (b - 1);
         }
-        __syncthreads();
-        T = s_T;
+        if (b == 0) {
+            uint32_t m1 = 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (j < nslots) m1 += __popcll(__ballot(c[j] >= (T | 1)));
+            if (m1 >= need) T |= 1;
+        }
     } else {
         int round = 0;
         for (int sh2 = 29; sh2 >= 1; sh2 -= 2, ++round) {
@@ -340,7 +344,6 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     }
 
     // ---- 3. ordered compaction
-    const uint64_t below = lanes_below(lane);
     uint32_t gt_w = 0, eq_w = 0, gt_tot_w = 0, eq_tot_w = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {

@@ -191,6 +191,38 @@ def test_edge_cases():
         check_output(widen(Y), Yref, Sabs, sel["kk"], f"edge M={M} K={K} N={N} gr={gr} r={r} act={act}")
 
 
+def test_select_large_threshold_buckets():
+    """Groups whose threshold bucket holds many keys: every score equal (all
+    K keys in one bucket, the search shared by the whole workgroup), 1500
+    columns of equal norm around the kk-th score, and a few hundred equal
+    columns; kept sets against the oracle, through rmm_select and
+    rmm_select_gather."""
+    rng = np.random.default_rng(17)
+    M, K, N, gr = 384, 4096, 64, 128
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    a[0:128] = 0.0                                     # group 0: every score 0
+    a[128:256, 1000:2500] = a[128:256, 7:8]            # group 1: 1500 equal columns
+    a[256:384, 3000:3300] = a[256:384, 5:6]            # group 2: 300 equal columns
+    A = up_bf16(synth.f32_to_bf16_bits(a))
+    B = up_bf16(synth.f32_to_bf16_bits(np.full((K, N), 0.25, np.float32)))
+    A64, B64 = widen(A), widen(B)
+    bnorm = rmm.rmm_rownorms(B)
+    for r in (0.3, 0.5, 0.7):
+        kk = rmm.rmm_kk(r, K)
+        sel = O.select(A64, r, gr, O.rownorms(B64))
+        idx = torch.zeros((3, rmm.rmm_kk_pad(kk)), dtype=torch.int32, device=DEV)
+        rmm.rmm_select(A, r, gr, bnorm=bnorm, idx=idx)
+        idx2, ap = rmm.rmm_select_gather(A, r, gr, bnorm=bnorm)
+        torch.cuda.synchronize()
+        ig = down(idx)
+        assert np.array_equal(ig[:, :kk], sel["idx"]), r
+        assert torch.equal(idx, idx2), r
+        pan = down(ap)
+        bits = synth.f32_to_bf16_bits(a)
+        for m in (0, 127, 128, 200, 383):
+            assert np.array_equal(pan[m, :kk], bits[m, ig[m // gr, :kk]]), (r, m)
+
+
 # ---------------------------------------------------------------- full sizes
 FULL = [("attn_proj", 0.3), ("attn_proj", 0.5), ("attn_proj", 0.7), ("attn_proj", 1.0),
         ("mlp_down", 0.5), ("mlp_down", 0.7), ("mlp_down", 0.9), ("mlp_down", 1.0),
