@@ -223,6 +223,29 @@ def test_select_large_threshold_buckets():
             assert np.array_equal(pan[m, :kk], bits[m, ig[m // gr, :kk]]), (r, m)
 
 
+@pytest.mark.parametrize("K", [32768, 32760], ids=lambda k: f"K{k}")
+def test_max_contraction(K):
+    """The largest K the selection takes (32 keys per thread), and a ragged one:
+    rows of 64 KiB are past the LDS-staged gather, so the gather reads A by
+    index; kept sets against the oracle, the panel exact, every output row
+    within the bound."""
+    M, N, gr, r = 200, 72, 128, 0.5
+    tag = f"max K={K}"
+    log(f"case {tag}")
+    c = make_case("attn_proj", M, K, N, seed=23)
+    bnorm = rmm.rmm_rownorms(c["B"])
+    idx, scores, thresh, bound, Ap, Y = run_chain(c, r, gr, bnorm)
+    sel, ig = check_selection(c, r, gr, bnorm, idx, scores, thresh, bound, tag)
+    kk = sel["kk"]
+    ap = down(Ap)
+    for m in (0, 127, 128, 199):
+        assert np.array_equal(ap[m, :kk], c["raw"]["A"][m, ig[m // gr, :kk]]), f"{tag}: panel row {m}"
+        assert np.all(ap[m, kk:] == 0)
+    Yref = O.reduced(c["A64"], c["B64"], ig, kk, gr)
+    Sabs = O.reduced(np.abs(c["A64"]), np.abs(c["B64"]), ig, kk, gr)
+    check_output(widen(Y), Yref, Sabs, kk, tag)
+
+
 # ---------------------------------------------------------------- full sizes
 FULL = [("attn_proj", 0.3), ("attn_proj", 0.5), ("attn_proj", 0.7), ("attn_proj", 1.0),
         ("mlp_down", 0.5), ("mlp_down", 0.7), ("mlp_down", 0.9), ("mlp_down", 1.0),
