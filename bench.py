@@ -12,8 +12,11 @@ lognormal channel scales, 1% outlier channels x20) times W 4096x4096 bf16
 `value` is the retained-K TFLOP/s of the whole step at r = 0.5
 (2*M*kk*N / step time); per-r stage times, GEMM-only TFLOP/s and the speed-ups
 over r = 1.0 are reported beside it.  Other workloads (--workload mlp_down,
-decode, decode_q8, pv4k, pv16k, tiny) use the same contract; decode_q8 is the
-decode shape on the int8 weight path (weights quantised once, before timing).
+decode, decode_q8, pv4k, pv16k, attn4k, attn16k, tiny) use the same contract;
+decode_q8 is the decode shape on the int8 weight path (weights quantised once,
+before timing); attn4k and attn16k are the attention chain (feature scores and
+selection, probabilities producer with the P.V key scores, key selection,
+reduced P.V) at L = 4096 and 16384.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -42,7 +45,8 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="attn_proj",
-                   choices=["attn_proj", "mlp_down", "decode", "decode_q8", "pv4k", "pv16k", "attn4k", "tiny"])
+                   choices=["attn_proj", "mlp_down", "decode", "decode_q8", "pv4k", "pv16k", "attn4k", "attn16k",
+                            "tiny"])
     p.add_argument("--ratios", type=str, default=None, help="comma-separated r values")
     p.add_argument("--headline-r", type=float, default=0.5)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -305,6 +309,8 @@ class Attn:
         self.idx_pv = torch.empty((self.H * self.G, rmm.rmm_kk_pad(L)), dtype=torch.int32, device=dev)
         self.O = torch.empty((self.H, L, self.D), dtype=torch.bfloat16, device=dev)
         self.qs = torch.empty((self.H, self.G, self.D), dtype=torch.float32, device=dev)
+        self.wsq = torch.empty(int(rmm.lib().rmm_qk_select_workspace_bytes(self.H, L, self.D, 128, 1)),
+                               dtype=torch.uint8, device=dev)
         need = int(rmm.lib().rmm_attn_probs_workspace_bytes(self.H, L, self.D, 1))
         self.wsp = torch.empty(need, dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
@@ -322,7 +328,8 @@ class Attn:
         if r >= 1.0:
             return [("probs", lambda: rmm.rmm_attn_probs(self.Q, self.K, None, 1.0, Pt=self.Pt)),
                     ("gemm", lambda: rmm.rmm_pv_gemm(self.Pt, self.V, 1.0, None, O=self.O))], self.D
-        return [("score", lambda: rmm.rmm_qk_select(self.Q, self.K, r, idx_out=self.idx_qk, scores_out=self.qs)),
+        return [("score", lambda: rmm.rmm_qk_select(self.Q, self.K, r, idx_out=self.idx_qk, scores_out=self.qs,
+                                                          ws=self.wsq)),
                 ("probs", lambda: rmm.rmm_attn_probs(self.Q, self.K, self.idx_qk, r, Pt=self.Pt, V=self.V,
                                                      pv_scores=self.pvs, ws=self.wsp)),
                 ("select", lambda: rmm.rmm_pv_select_scores(self.pvs, r, idx_out=self.idx_pv)),
@@ -554,8 +561,8 @@ def main():
         copy_calibration(torch, args.copy_calibration, dev)
     if args.workload in ("pv4k", "pv16k"):
         W = PV(4096 if args.workload == "pv4k" else 16384, dev)
-    elif args.workload == "attn4k":
-        W = Attn(4096, dev)
+    elif args.workload in ("attn4k", "attn16k"):
+        W = Attn(4096 if args.workload == "attn4k" else 16384, dev)
     else:
         W = Linear(args.workload, dev)
     ratios = [float(x) for x in args.ratios.split(",")] if args.ratios else list(W.ratios)
@@ -603,7 +610,7 @@ def main():
         groups = args.cpu_groups
         if groups is None:
             groups = {"attn_proj": 24, "mlp_down": 1, "decode": 1, "decode_q8": 1, "tiny": 1, "pv4k": 8,
-                      "pv16k": 2, "attn4k": 32}[W.name]
+                      "pv16k": 2, "attn4k": 32, "attn16k": 4}[W.name]
         log(f"[bench] oracle baseline on {groups} groups ...")
         cpu = W.cpu_baseline(headline, groups)
         log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s ({cpu['seconds']} s)")

@@ -281,7 +281,10 @@ int rmm_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq, c
  * features are kept (ties to the lower index) and written ascending to
  * idx_out[h*G + g][0 .. kk-1], padded by repeating the last one up to
  * rmm_kk_pad(kk).  0 < r <= 1; ldidx_out % 4 == 0, >= rmm_kk_pad(D).
- * scores_out [H][G][D] binary32 or NULL (then the workspace holds them). */
+ * scores_out [H][G][D] binary32 or NULL (then the workspace holds them).
+ * The workspace (rmm_qk_select_workspace_bytes, 16-byte aligned, device)
+ * always holds the binary64 key sums of squares, H*G*D*8 bytes rounded up to
+ * 256, followed by the scores when scores_out is NULL. */
 size_t rmm_qk_select_workspace_bytes(int64_t H, int64_t L, int64_t D, int64_t qblock, int have_scores_out);
 int rmm_qk_select(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int64_t D, double r,
                   int64_t qblock, int causal, int use_k, int32_t *idx_out, int64_t ldidx_out,

@@ -391,9 +391,11 @@ extern "C" {
 
 size_t rmm_qk_select_workspace_bytes(int64_t H, int64_t L, int64_t D, int64_t qblock, int have_scores_out)
 {
-    if (H < 1 || L < 1 || D < 1 || qblock < 1 || have_scores_out) return 0;
+    if (H < 1 || L < 1 || D < 1 || qblock < 1) return 0;
     const int64_t G = (L + qblock - 1) / qblock;
-    return align_up((size_t)H * G * D * sizeof(float));
+    size_t n = align_up((size_t)H * G * D * sizeof(double));   // key sums of squares
+    if (!have_scores_out) n += align_up((size_t)H * G * D * sizeof(float));
+    return n;
 }
 
 int rmm_qk_select(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int64_t D, double r,
@@ -409,8 +411,12 @@ int rmm_qk_select(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, in
     if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
     hipStream_t s = as_stream(stream);
     const int64_t G = (L + qblock - 1) / qblock;
-    float *sc = scores_out ? scores_out : (float *)ws;
-    if (hipError_t e = launch_qk_score(Q, K, H, L, causal ? 1 : 0, use_k ? 1 : 0, sc, s)) return hip_status(e);
+    char *w = (char *)ws;
+    double *ksum = (double *)w;
+    w += align_up((size_t)H * G * D * sizeof(double));
+    float *sc = scores_out ? scores_out : (float *)w;
+    if (hipError_t e = launch_qk_score(Q, K, H, L, causal ? 1 : 0, use_k ? 1 : 0, ksum, sc, s))
+        return hip_status(e);
     SelectShape sh{};
     sh.groups = H * G;
     sh.K = D;

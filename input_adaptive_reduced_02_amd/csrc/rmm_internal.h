@@ -107,7 +107,7 @@ hipError_t launch_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int6
                           int64_t kk, int64_t group_rows, void *Y, int ydt, int64_t ldy, void *ws, hipStream_t s);
 hipError_t launch_pv_vnorm(const uint16_t *V, int64_t H, int64_t L, int64_t D, double *vnorm, hipStream_t s);
 hipError_t launch_qk_score(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int causal, int use_k,
-                           float *scores, hipStream_t s);
+                           double *ksum, float *scores, hipStream_t s);
 hipError_t launch_attn_probs(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int causal,
                              const int32_t *idx, int64_t ldidx, int64_t kk, uint16_t *Pt, const double *vnorm,
                              float *pvs, hipStream_t s);

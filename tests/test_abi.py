@@ -207,8 +207,9 @@ def test_validation_rejects_bad_arguments():
     assert L.rmm_gemm_q8(P, 64, P2, 32, P3, None, 0, 64, 32, 64, 64, P3, BF, 32, P3, 16, None) == EINVAL   # short ws
     # qk_select(Q, K, H, L, D, r, qblock, causal, use_k, idx, ldidx, scores, ws, wsb, stream)
     QW = L.rmm_qk_select_workspace_bytes(2, 256, 128, 128, 0)
-    assert QW == 2 * 2 * 128 * 4
-    assert L.rmm_qk_select_workspace_bytes(2, 256, 128, 128, 1) == 0
+    # the key sums of squares always (2 heads x 2 blocks x 128 doubles), the scores unless given
+    assert L.rmm_qk_select_workspace_bytes(2, 256, 128, 128, 1) == 4096
+    assert QW == 4096 + 2048
     assert L.rmm_qk_select(None, P2, 2, 256, 128, 0.5, 128, 1, 1, P3, 128, None, P3, QW, None) == EINVAL
     assert L.rmm_qk_select(P, P2, 2, 256, 128, 0.0, 128, 1, 1, P3, 128, None, P3, QW, None) == EINVAL    # r
     assert L.rmm_qk_select(P, P2, 2, 256, 128, nan, 128, 1, 1, P3, 128, None, P3, QW, None) == EINVAL
