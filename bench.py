@@ -365,10 +365,17 @@ class Attn:
         import numpy as np
 
         import oracle as O
-        Q0, K0, V0 = (O.widen_bf16(x[0]) for x in (self.q_bits, self.k_bits, self.v_bits))
+        groups = min(groups, self.H * self.G)
+        heads = {}
         fl = 0.0
         t0 = time.perf_counter()
-        for g in range(self.G - 1, max(-1, self.G - 1 - groups), -1):
+        for i in range(groups):
+            # the query blocks of head 0, heaviest first, then those of head 1, ...
+            h, g = i // self.G, self.G - 1 - i % self.G
+            if h not in heads:
+                heads.clear()
+                heads[h] = tuple(O.widen_bf16(x[h]) for x in (self.q_bits, self.k_bits, self.v_bits))
+            Q0, K0, V0 = heads[h]
             sel = O.qk_select_block(Q0, K0, 128, g, r, True, True)
             P = O.attn_probs(Q0, K0, g * 128, 128, True, sel["idx"])
             Kg = min(self.L, 128 * (g + 1))
@@ -379,8 +386,9 @@ class Attn:
             fl += 2.0 * 128 * Kg * sel["kk"] + 2.0 * 128 * kk * self.D
         dt = time.perf_counter() - t0
         return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
-                    sample=f"{groups} query blocks of head 0 (the last ones) at r={r}: feature scores + select + "
-                           f"probabilities + key scores + select + reduced P.V, {fl / 1e9:.2f} GFLOP in {dt:.1f} s",
+                    sample=f"{groups} query blocks (per head from the last, heads in order) at r={r}: "
+                           f"feature scores + select + probabilities + key scores + select + reduced P.V, "
+                           f"{fl / 1e9:.2f} GFLOP in {dt:.1f} s",
                     seconds=round(dt, 2))
 
 
@@ -610,7 +618,7 @@ def main():
         groups = args.cpu_groups
         if groups is None:
             groups = {"attn_proj": 24, "mlp_down": 1, "decode": 1, "decode_q8": 1, "tiny": 1, "pv4k": 8,
-                      "pv16k": 2, "attn4k": 32, "attn16k": 4}[W.name]
+                      "pv16k": 2, "attn4k": 512, "attn16k": 96}[W.name]
         log(f"[bench] oracle baseline on {groups} groups ...")
         cpu = W.cpu_baseline(headline, groups)
         log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s ({cpu['seconds']} s)")
