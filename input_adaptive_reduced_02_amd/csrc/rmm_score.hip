@@ -138,17 +138,45 @@ hipError_t launch_colscore(const void *A, int dt, int64_t M, int64_t K, int64_t 
 }
 
 // ------------------------------------------------------------------ P.V scores
-// ||V[h][k][:]||_2 for every key: lane per key, ascending d, exact squares.
-__global__ void __launch_bounds__(256)
-k_pv_vnorm(const uint16_t *__restrict__ V, int64_t HL, int64_t D, double *__restrict__ vnorm)
+// ||V[h][k][:]||_2 for every key (head dimension 128): one wave per 64 keys.
+// The 64 rows (16 KiB) arrive with coalesced 16-byte loads (one 1 KiB run,
+// four rows, per instruction) and pass through LDS, so that lane l then sums
+// row l's squares in ascending d in binary64 (exact squares, one rounding per
+// fma) -- the sequential order.  Rows are staged 272 bytes apart, so the 16
+// lanes of one ds_read_b128 phase touch distinct banks.
+constexpr int kVnPitch = 272;
+
+__device__ __forceinline__ void wave_lds_fence()
 {
-    const int64_t hk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (hk >= HL) return;
-    const uint16_t *vrow = V + hk * D;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ void __launch_bounds__(256)
+k_pv_vnorm(const uint16_t *__restrict__ V, int64_t HL, double *__restrict__ vnorm)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char st[4][64 * kVnPitch];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * 64;   // this wave's first key
+    if (r0 >= HL) return;                                        // no workgroup barrier below
+    unsigned char *s = st[wave];
+    u32x4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        int64_t row = r0 + 4 * i + (lane >> 4);
+        if (row > HL - 1) row = HL - 1;
+        v[i] = *(const u32x4 *)(V + row * 128 + 8 * (lane & 15));
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) *(u32x4 *)(s + (4 * i + (lane >> 4)) * kVnPitch + 16 * (lane & 15)) = v[i];
+    wave_lds_fence();
+    const int64_t row = r0 + lane;
+    if (row >= HL) return;
     double vv = 0.0;
-    for (int64_t d = 0; d < D; d += 8) {
-        const uint4 v = *(const uint4 *)(vrow + d);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const u32x4 w = *(const u32x4 *)(s + lane * kVnPitch + 16 * c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const double lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
@@ -156,7 +184,7 @@ k_pv_vnorm(const uint16_t *__restrict__ V, int64_t HL, int64_t D, double *__rest
             vv = __builtin_fma(hi, hi, vv);
         }
     }
-    vnorm[hk] = __builtin_sqrt(vv);
+    vnorm[row] = __builtin_sqrt(vv);
 }
 
 // Block masses times V norms.  Work item = (head h, query block g, 64 keys
@@ -302,16 +330,16 @@ k_pv_mass(const uint16_t *__restrict__ Pt, int64_t H, int64_t L, int64_t qblock,
 
 hipError_t launch_pv_vnorm(const uint16_t *V, int64_t H, int64_t L, int64_t D, double *vnorm, hipStream_t s)
 {
+    if (D != 128) return hipErrorInvalidValue;   // the callers take D == 128 only
     const int64_t HL = H * L;
-    hipLaunchKernelGGL(k_pv_vnorm, dim3((unsigned)((HL + 255) / 256)), dim3(256), 0, s, V, HL, D, vnorm);
+    hipLaunchKernelGGL(k_pv_vnorm, dim3((unsigned)((HL + 255) / 256)), dim3(256), 0, s, V, HL, vnorm);
     return hipGetLastError();
 }
 
 hipError_t launch_pv_score(const uint16_t *Pt, const uint16_t *V, int64_t H, int64_t L, int64_t D,
                            int64_t qblock, int causal, double *vnorm, float *scores, hipStream_t s)
 {
-    const int64_t HL = H * L;
-    hipLaunchKernelGGL(k_pv_vnorm, dim3((unsigned)((HL + 255) / 256)), dim3(256), 0, s, V, HL, D, vnorm);
+    if (hipError_t e = launch_pv_vnorm(V, H, L, D, vnorm, s)) return e;
     const int64_t G = (L + qblock - 1) / qblock;
     const int64_t cpb = (L + 63) / 64;
     // items per head: causal blocks hold 2(g+1) items, the last ceil(L/64) - 2(G-1)
