@@ -617,8 +617,8 @@ def main():
     if not args.no_cpu_baseline:
         groups = args.cpu_groups
         if groups is None:
-            groups = {"attn_proj": 24, "mlp_down": 1, "decode": 1, "decode_q8": 1, "tiny": 1, "pv4k": 8,
-                      "pv16k": 2, "attn4k": 512, "attn16k": 96}[W.name]
+            groups = {"attn_proj": 24, "mlp_down": 1, "decode": 1, "decode_q8": 1, "tiny": 1, "pv4k": 32,
+                      "pv16k": 128, "attn4k": 512, "attn16k": 96}[W.name]
         log(f"[bench] oracle baseline on {groups} groups ...")
         cpu = W.cpu_baseline(headline, groups)
         log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s ({cpu['seconds']} s)")
