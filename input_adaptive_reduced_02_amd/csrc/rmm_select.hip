@@ -29,15 +29,17 @@
 //      16 waves share the search through LDS.
 // Then the ordered compaction: per-wave exclusive counts of keys > T and == T
 // come from ballots masked to the lower lanes, per-wave totals from one LDS
-// exchange; keys == T are kept in index order until kk.  No atomics decide an
-// order and no floating-point sum decides anything, so the output is
-// deterministic.
+// exchange; keys == T are kept in index order until kk.  Atomics only place
+// the candidates in LDS, whose order T does not depend on; no atomic decides
+// an output order and no floating-point sum decides anything, so the output
+// is deterministic.
 //
 // Select + gather in one launch (NRB > 0): the group's rows are split over
 // `slices` workgroups, each of which runs the whole selection of its group
 // (identical, deterministic work) while its own rows of A stream into LDS
 // with DMA loads (issued after the histogram, in flight during the rest of
-// the selection).  After the threshold and the ordered compaction (kept
+// the selection; issued before the keys arrive they delayed them and were
+// slower).  After the threshold and the ordered compaction (kept
 // indices into an LDS list) every workgroup picks its rows' kept elements out
 // of LDS into the bf16 panel, 8 per lane and one 16-byte store; the first
 // slice also writes the index row, threshold and bound.  The panel equals the
@@ -108,9 +110,6 @@ __device__ __forceinline__ uint64_t count3(const int32_t *cand, uint32_t first, 
     return (uint64_t)m1 | ((uint64_t)m2 << 21) | ((uint64_t)m3 << 42);
 }
 
-// NRB = 0: selection only, one workgroup per group.  NRB > 0: selection and
-// gather, `ga.slices` workgroups per group, each staging at most NRB 1 KiB
-// blocks of rows per wave (16 * NRB KiB per workgroup).
 // DMA: every lane copies 16 bytes from its global address to LDS[lds + 16*lane]
 // (global_load_lds_dwordx4; no register result, so nothing waits for it until
 // an explicit s_waitcnt).
@@ -122,6 +121,9 @@ __device__ __forceinline__ uint32_t sel_lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
+// NRB = 0: selection only, one workgroup per group.  NRB > 0: selection and
+// gather, `ga.slices` workgroups per group, each staging at most NRB 1 KiB
+// blocks of rows per wave (16 * NRB KiB per workgroup).
 template <int KPT, int NRB>
 __global__ void __launch_bounds__(kSelectThreads)
 k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__ idx, int64_t ldidx,
