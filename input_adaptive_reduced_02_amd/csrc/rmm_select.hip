@@ -437,8 +437,9 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
 #pragma unroll
                 for (int q = 0; q < 8; ++q) h[q] = (j0 + q < kk32) ? row[cand[j0 + q]] : 0u;
             }
-            *(uint4 *)(ga.Ap + (srow0 + i) * ga.ldp + j0) =
-                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            // streaming store: the panel is read next by other CUs, not from this L2
+            const u32x4 o = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+            __builtin_nontemporal_store(o, (u32x4 *)(ga.Ap + (srow0 + i) * ga.ldp + j0));
         }
     }
 }
