@@ -267,8 +267,9 @@ k_gemm_dl(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
         for (int e = threadIdx.x; e < TM * (TN / 8); e += NT) {
             const int r = e / (TN / 8), ch = e % (TN / 8);
             const int64_t row = row0 + r, col = col0 + 8 * ch;
-            if (row < row_end && col < N)
-                *(uint4 *)((uint16_t *)Y + row * ldy + col) = *(const uint4 *)(st + r * PITCH + 16 * ch);
+            if (row < row_end && col < N)   // streaming stores: Y is not read back by this launch
+                __builtin_nontemporal_store(*(const u32x4 *)(st + r * PITCH + 16 * ch),
+                                            (u32x4 *)((uint16_t *)Y + row * ldy + col));
         }
         return;
     }
