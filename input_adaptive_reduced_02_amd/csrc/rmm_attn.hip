@@ -500,7 +500,10 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                         const int c = first + stride * i, r = c >> 4, qc = c & 15;
                         const int64_t k = kp0 + r;
                         if (k < Kvalid && 8 * qc < nq)
-                            *(u32x4 *)(Pt + (h * L + k) * L + q0 + 8 * qc) = *(const u32x4 *)&pb[r * kPitch + 8 * qc];
+                            // non-temporal: P is written once and read by the next launch, so
+                            // it should not displace the K and Q tiles still being reused
+                            __builtin_nontemporal_store(*(const u32x4 *)&pb[r * kPitch + 8 * qc],
+                                                        (u32x4 *)(Pt + (h * L + k) * L + q0 + 8 * qc));
                     }
                 };
                 if (!PVS) {
