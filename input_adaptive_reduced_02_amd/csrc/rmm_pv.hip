@@ -57,6 +57,12 @@ __device__ __forceinline__ void pv_dma16(const void *g, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
+// the same with the non-temporal policy, for P rows: each is read once, and keeping them
+// out of the caches leaves room for the V rows that other query blocks of the head reuse
+__device__ __forceinline__ void pv_dma16_nt(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+}
 __device__ __forceinline__ void pv_dma4(const void *g, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
@@ -139,7 +145,7 @@ k_pv_gemm(const uint16_t *__restrict__ Pt, const uint16_t *__restrict__ V, int64
         for (int i = 0; i < A_SHARE; ++i) {
             const int jr = (wave * A_SHARE + i) * 4 + (lane >> 4);
             const int64_t key = (kbase + jr < kk) ? kr[i] : 0;   // past kk: key 0, P cleared in registers
-            pv_dma16(p_src[i] + key * L, sp + (wave * A_SHARE + i) * 1024);
+            pv_dma16_nt(p_src[i] + key * L, sp + (wave * A_SHARE + i) * 1024);
             pv_dma16(v_src[i] + key * 128, sv + (wave * A_SHARE + i) * 1024);
         }
     };
