@@ -69,6 +69,13 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
+// the same with the non-temporal policy, for operand rows a launch reads exactly once
+// (the decode GEMMs' kept B rows): they stream past the caches instead of evicting
+// what is reused
+__device__ __forceinline__ void dma16_nt(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void *g, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");

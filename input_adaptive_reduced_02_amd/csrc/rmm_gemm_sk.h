@@ -130,7 +130,7 @@ k_gemm_sk(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
 #pragma unroll
         for (int i = 0; i < S::A_SHARE; ++i) dma16(a_src[i] + abase, sa + (wave * S::A_SHARE + i) * 1024);
 #pragma unroll
-        for (int i = 0; i < S::B_SHARE; ++i) dma16(brow[i], sb + (wave * S::B_SHARE + i) * 1024);
+        for (int i = 0; i < S::B_SHARE; ++i) dma16_nt(brow[i], sb + (wave * S::B_SHARE + i) * 1024);
     };
 
     floatx16 acc[FM];

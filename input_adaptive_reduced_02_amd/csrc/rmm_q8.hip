@@ -308,7 +308,7 @@ k_gemm_q8(const uint16_t *__restrict__ A, int64_t lda, const int8_t *__restrict_
         for (int b = 0; b < S::B_BLOCKS; ++b) {
             const int jr = b * S::B_ROWS_PER_BLOCK + lane / S::B_CHUNKS;
             const int64_t krow = (i < n && kbase + jr < kk) ? kr[b] : 0;   // past the end: row 0
-            dma16(b_src[b] + krow * ldq, sb + b * 1024);
+            dma16_nt(b_src[b] + krow * ldq, sb + b * 1024);
         }
     };
 
