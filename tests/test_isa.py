@@ -6,7 +6,11 @@
   build disables it, this makes sure it stays disabled;
 * m0 is written only by the DMA sequences (s_mov_b32 m0, sN directly followed
   by a global_load_lds_*), so nothing else relies on its value;
-* every kernel's static LDS fits one CU (160 KiB).
+* every kernel's static LDS fits one CU (160 KiB);
+* the streams a launch touches once keep their non-temporal policy (the `nt`
+  modifier): the attention producer's P stores, the P.V kernel's P loads, the
+  decode GEMMs' kept-row loads, the prefill GEMM's Y stores and the fused
+  select+gather's panel stores.
 """
 import concurrent.futures as cf
 import os
@@ -86,3 +90,36 @@ def test_m0_only_feeds_dma(device_asm):
             if re.search(r"\bm0\b", ln) and not ln.startswith("global_load_lds"):
                 assert re.match(r"s_mov_b32 m0, s\d+$", ln), (src, ln)
                 assert lines[i + 1].startswith("global_load_lds"), (src, ln, lines[i + 1])
+
+
+def kernel_bodies(asm, part):
+    """{mangled name: body} for every kernel whose mangled name contains `part`."""
+    out = {}
+    for m in re.finditer(r"^(_Z\S*" + part + r"\S*):[^\n]*$", asm, re.M):
+        end = asm.find(".Lfunc_end", m.end())
+        out[m.group(1)] = asm[m.end():end]
+    return out
+
+
+# (source, kernel, instruction, every instantiation or at least one): the
+# prefill GEMM's non-bf16 epilogue and the select kernels without a fused
+# gather have no such stream
+NT_STREAMS = [
+    ("rmm_attn.hip", "k_attn_probs", "global_store_dwordx4", True),
+    ("rmm_pv.hip", "k_pv_gemm", "global_load_lds_dwordx4", True),
+    ("rmm_gemm.hip", "k_gemm_sk", "global_load_lds_dwordx4", True),
+    ("rmm_q8.hip", "k_gemm_q8", "global_load_lds_dwordx4", True),
+    ("rmm_gemm.hip", "k_gemm_dl", "global_store_dwordx4", False),
+    ("rmm_select.hip", "k_select", "global_store_dwordx4", False),
+]
+
+
+@pytest.mark.parametrize("src,kernel,insn,every", NT_STREAMS, ids=[f"{k}-{i}" for _, k, i, _ in NT_STREAMS])
+def test_nontemporal_streams(device_asm, src, kernel, insn, every):
+    bodies = kernel_bodies(device_asm[src], kernel)
+    assert bodies, f"no {kernel} in {src}"
+    has = {name: bool(re.search(r"^\s*" + insn + r"\b[^\n]*\bnt\b", body, re.M)) for name, body in bodies.items()}
+    if every:
+        assert all(has.values()), [n for n, v in has.items() if not v]
+    else:
+        assert any(has.values()), list(has)
