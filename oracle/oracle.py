@@ -65,6 +65,10 @@ def _declare(lib):
     lib.oracle_reduced_entries.argtypes = [_D, _L, _D, _L, _L, _I32, _L, _L, _I64, _I64, _L, _D]
     lib.oracle_bound.restype = ctypes.c_double
     lib.oracle_bound.argtypes = [_D, _L, _I32, _L]
+    lib.oracle_thresh.restype = ctypes.c_float
+    lib.oracle_thresh.argtypes = [_F, _I32, _L]
+    lib.oracle_near_ties.restype = _L
+    lib.oracle_near_ties.argtypes = [_D, _F, _L, _I32, _L, ctypes.c_double, _I32]
     lib.oracle_pv_prefix.restype = _L
     lib.oracle_pv_prefix.argtypes = [_L, _L, _L, ctypes.c_int]
     lib.oracle_pv_scores.restype = None
@@ -156,20 +160,32 @@ def topk(s32, kk_, lib=None):
     return out
 
 
-def near_ties(s64_row, s32_row, idx):
-    """Indices whose unrounded score lies within NEAR_TIE_REL of the k-th score."""
-    kept32 = s32_row[idx]
-    last = idx[kept32 == kept32.min()].max()  # the kk-th element of the rank order
-    t = s64_row[last]
-    band = np.abs(s64_row - t) <= NEAR_TIE_REL * abs(t)
-    return np.nonzero(band)[0]
+def thresh(s32_row, idx, lib=None):
+    """The binary32 score of rank kk (the smallest key among the kept idx)."""
+    lib = lib or load()
+    s = np.ascontiguousarray(s32_row, dtype=np.float32)
+    i = np.ascontiguousarray(idx, dtype=np.int32)
+    return np.float32(lib.oracle_thresh(_p(s, _F), _p(i, _I32), len(i)))
+
+
+def near_ties(s64_row, s32_row, idx, rel=NEAR_TIE_REL, lib=None):
+    """Ascending indices whose unrounded score lies within `rel` (relative) of
+    the unrounded score of the rank-kk element."""
+    lib = lib or load()
+    s64 = _f64(s64_row)
+    s32 = np.ascontiguousarray(s32_row, dtype=np.float32)
+    i = np.ascontiguousarray(idx, dtype=np.int32)
+    out = np.empty(len(s64), np.int32)
+    n = lib.oracle_near_ties(_p(s64, _D), _p(s32, _F), len(s64), _p(i, _I32), len(i), float(rel), _p(out, _I32))
+    return out[:n].copy()
 
 
 def select(A, r, group_rows, b=None, lib=None):
     """The whole selection step for a linear layer.
 
     Returns dict(kk, idx [G, kk] ascending, s64, s32, thresh [G] (binary32 k-th
-    score), bound [G] (sum of dropped unrounded scores), near [list of arrays]).
+    score), bound [G] (sum of dropped unrounded scores), near [list of arrays]:
+    each group's near-tie band, logged by the GPU tests).
     """
     lib = lib or load()
     A = _f64(A)
@@ -180,16 +196,16 @@ def select(A, r, group_rows, b=None, lib=None):
     s64, s32 = scores(A, group_rows, b, lib)
     G = s64.shape[0]
     idx = np.empty((G, kk_), np.int32)
-    thresh = np.empty(G, np.float32)
+    th = np.empty(G, np.float32)
     bound = np.empty(G, np.float64)
     near = []
     for g in range(G):
         idx[g] = topk(s32[g], kk_, lib)
-        thresh[g] = s32[g][idx[g]].min()
+        th[g] = thresh(s32[g], idx[g], lib)
         row = np.ascontiguousarray(s64[g])
         bound[g] = lib.oracle_bound(_p(row, _D), K, _p(idx[g], _I32), kk_)
-        near.append(near_ties(s64[g], s32[g], idx[g]))
-    return dict(kk=kk_, idx=idx, s64=s64, s32=s32, thresh=thresh, bound=bound, near=near)
+        near.append(near_ties(s64[g], s32[g], idx[g], lib=lib))
+    return dict(kk=kk_, idx=idx, s64=s64, s32=s32, thresh=th, bound=bound, near=near)
 
 
 def reduced(A, B, idx, kk_, group_rows, m0=0, m1=None, lib=None):
@@ -295,7 +311,7 @@ def pv_select_block(Pt, V, L, qblock, g, r, causal=True, lib=None):
     kk_ = kk(r, Kg, lib)
     idx = topk(s32, kk_, lib)
     return dict(Kg=Kg, kk=kk_, idx=idx, s64=s64, s32=s32, Ptb=Ptb, V=Vg,
-                near=near_ties(s64, s32, idx))
+                near=near_ties(s64, s32, idx, lib=lib))
 
 
 # ---------------------------------------------------------------- QK^T and the probabilities
@@ -322,7 +338,7 @@ def qk_select_block(Q, K, qblock, g, r, causal=True, use_k=True, lib=None):
     s64, s32 = qk_scores(Q, K, q0, nq, Kg, use_k, lib)
     kk_ = kk(r, D, lib)
     idx = topk(s32, kk_, lib)
-    return dict(Kg=Kg, kk=kk_, idx=idx, s64=s64, s32=s32, near=near_ties(s64, s32, idx))
+    return dict(Kg=Kg, kk=kk_, idx=idx, s64=s64, s32=s32, near=near_ties(s64, s32, idx, lib=lib))
 
 
 def attn_probs(Q, K, q0, nq, causal=True, idx=None, lib=None):
@@ -380,6 +396,6 @@ def rownorms_q8(q, scale, lib=None):
 __all__ = [
     "load", "widen_bf16", "widen_f32", "kk", "rownorms", "colnorms", "scores", "topk", "select",
     "reduced", "reduced_entries", "dense", "bound", "pv_prefix", "pv_block_inputs", "pv_scores",
-    "pv_block", "pv_bound", "pv_select_block", "near_ties", "NEAR_TIE_REL",
+    "pv_block", "pv_bound", "pv_select_block", "near_ties", "thresh", "NEAR_TIE_REL",
     "quantize_q8", "dequant_q8", "rownorms_q8", "qk_scores", "qk_select_block", "attn_probs",
 ]

@@ -231,6 +231,41 @@ double oracle_bound(const double *s64, int64_t K, const int32_t *idx, int64_t kk
     return beta;
 }
 
+/* ---- threshold of one group (reading R4): the score of rank kk in the order
+ * (score descending, index ascending), which is the smallest binary32 key
+ * among the kept indices idx[0 .. kk-1]. */
+float oracle_thresh(const float *s32, const int32_t *idx, int64_t kk)
+{
+    float t = s32[idx[0]];
+    for (int64_t j = 1; j < kk; ++j)
+        if (s32[idx[j]] < t)
+            t = s32[idx[j]];
+    return t;
+}
+
+/* ---- near-tie band of one group.  The element of rank kk is the kept index
+ * with the smallest binary32 key, and among kept indices sharing that key the
+ * highest one (lower indices rank first).  t is its unrounded score; the band
+ * is every k in [0, K) with |s64[k] - t| <= rel * |t|, written ascending to
+ * out.  Returns the band's size.  Within the band a kept set may legitimately
+ * differ when the two sides' keys are not bit-identical. */
+int64_t oracle_near_ties(const double *s64, const float *s32, int64_t K, const int32_t *idx,
+                         int64_t kk, double rel, int32_t *out)
+{
+    int32_t last = idx[0];
+    for (int64_t j = 1; j < kk; ++j) {
+        int32_t i = idx[j];
+        if (s32[i] < s32[last] || (s32[i] == s32[last] && i > last))
+            last = i;
+    }
+    double t = s64[last];
+    int64_t n = 0;
+    for (int64_t k = 0; k < K; ++k)
+        if (fabs(s64[k] - t) <= rel * fabs(t))
+            out[n++] = (int32_t)k;
+    return n;
+}
+
 /* ---- P.V ("Escopo de Aplicacao": the token dimension of PV), reading R5.
  * P is stored key-major: Pt[k*L + q] = P[q, k].  The functions below see one
  * head and one query block: Ptb[k*ldp + i] = P[q0 + i, k] for i < nq. */

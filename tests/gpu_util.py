@@ -66,14 +66,19 @@ def check_output(y_gpu, y_ref, s_abs, kk, tag, f32_inputs=False):
 
 
 def compare_sets(idx_gpu, sel, g, kk, tag):
-    """Kept sets must match exactly; a difference is only tolerated inside the
-    near-tie band of the oracle (then it is logged)."""
+    """Kept sets must match the oracle's exactly.  Every caller first asserts
+    that the GPU's binary32 keys equal the oracle's bit for bit, and the
+    selection is a deterministic function of those keys (score descending,
+    ties to the lower index), so any difference is a selection bug, inside the
+    near-tie band or not.  The oracle's near-tie band is only logged, as the
+    acceptance rule asks."""
     a = np.asarray(idx_gpu[:kk])
     b = sel["idx"][g]
-    if np.array_equal(a, b):
-        return True
-    diff = np.setxor1d(a, b)
-    near = set(sel["near"][g].tolist())
-    log(f"  {tag} group {g}: {len(diff)} indices differ: {diff[:10]} (near-tie band {sorted(near)[:10]})")
-    assert set(diff.tolist()) <= near, f"{tag} group {g}: set differs outside the near-tie band"
-    return False
+    near = sel["near"][g]
+    if len(near) > 1:
+        log(f"  {tag} group {g}: {len(near)} indices in the near-tie band {near[:8].tolist()}")
+    if not np.array_equal(a, b):
+        diff = np.setxor1d(a, b)
+        raise AssertionError(f"{tag} group {g}: kept set differs from the oracle at {diff[:10].tolist()} "
+                             f"(near-tie band {near[:10].tolist()})")
+    return True

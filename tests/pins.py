@@ -330,6 +330,60 @@ def pin_hand_examples(lib):
     assert list(selt["idx"][0]) == t["I"]
 
 
+def pin_thresh_near_ties_hand(lib):
+    """The threshold and the near-tie band against tests/golden/hand_near_ties.txt:
+    scores at 0.9e-6 and 1.1e-6 relative of the rank-kk score, exact ties, a
+    zero threshold, two scores sharing one binary32 key, and the band centred
+    on the unrounded score; case 1 again at two power-of-two scales."""
+    g = read_golden("hand_near_ties.txt")
+    cases = [("s1", "1a"), ("s1", "1b"), ("s1", "1c"), ("s3", "3a"), ("s3", "3b"), ("s4", "4a"), ("s4", "4b"),
+             ("s5", "5")]
+    for c in ("1a", "1b", "1c"):
+        for sc in g["scale2"]:
+            cases.append((("s1", sc), c))
+    for src, c in cases:
+        scale = 1.0
+        if isinstance(src, tuple):
+            src, scale = src
+        s64 = np.array(g[src], float) * scale
+        s32 = s64.astype(np.float32)
+        kk = g[f"kk{c}"]
+        idx = O.topk(s32, kk, lib)
+        assert list(idx) == g[f"I{c}"], (c, scale, list(idx))
+        t = O.thresh(s32, idx, lib)
+        assert t == np.float32(g[f"T{c}"] * scale), (c, scale, t)
+        band = O.near_ties(s64, s32, idx, lib=lib)
+        assert list(band) == g[f"band{c}"], (c, scale, list(band))
+
+
+def pin_thresh_near_ties_sort(lib):
+    """On random scores with repeats and zeros: T is the kk-th largest binary32
+    key by numpy's sort; the band holds every slice whose unrounded score equals
+    the rank-kk slice's (band width 0) and lies inside [T-, T+] of any wider
+    band; every slice with a key strictly between the kept and dropped extremes
+    is ordered as the band says."""
+    rng = _rng(41)
+    for trial in range(40):
+        K = int(rng.integers(2, 300))
+        s64 = rng.lognormal(0, 2, K)
+        s64[rng.integers(0, K, K // 5)] = 0.0
+        rep = rng.integers(0, K, K // 4)
+        s64[rep] = s64[rng.integers(0, K)]
+        s32 = s64.astype(np.float32)
+        kk = int(rng.integers(1, K + 1))
+        idx = O.topk(s32, kk, lib)
+        t = O.thresh(s32, idx, lib)
+        assert t == np.sort(s32)[::-1][kk - 1]
+        # the rank-kk slice by the rank definition (stable argsort on (-key, index))
+        order = np.lexsort((np.arange(K), -s32.astype(np.float64)))
+        last = order[kk - 1]
+        b0 = O.near_ties(s64, s32, idx, rel=0.0, lib=lib)
+        assert list(b0) == list(np.nonzero(s64 == s64[last])[0])
+        b = O.near_ties(s64, s32, idx, lib=lib)
+        assert last in b and np.all(np.diff(b) > 0)
+        assert set(b0) <= set(b)
+
+
 # ------------------------------------------------------------------ P.V
 def _causal_probs(rng, L):
     logits = rng.standard_normal((L, L))
@@ -579,6 +633,7 @@ ALL_PINS = [
     pin_kk_exact_rational, pin_kk_golden, pin_norms_numpy, pin_scores_numpy, pin_topk_argsort,
     pin_topk_invariants, pin_topk_bruteforce, pin_select_nesting, pin_reduced_numpy,
     pin_dense_numpy, pin_reduced_exact, pin_bound, pin_closed_forms, pin_hand_examples,
+    pin_thresh_near_ties_hand, pin_thresh_near_ties_sort,
     pin_pv_numpy, pin_pv_hand, pin_q8_hand, pin_q8_rounding, pin_q8_dequant_norms,
     pin_qk_hand, pin_qk_scores, pin_attn_probs,
 ]

@@ -39,6 +39,14 @@ MUTANTS = [
     ("reduced_transposed_B", "void oracle_reduced", [("y[n] += a * brow[n];", "y[n] += a * B[(n % ldb) * ldb + (k % ldb)];")]),
     ("entries_wrong_row", "void oracle_reduced_entries", [("A[m * lda + k]", "A[(m / group_rows) * group_rows * lda + k]")]),
     ("bound_sums_kept", "double oracle_bound", [("if (!kept[k])", "if (kept[k])")]),
+    ("thresh_is_max", "float oracle_thresh", [("if (s32[idx[j]] < t)", "if (s32[idx[j]] > t)")]),
+    ("thresh_first_kept", "float oracle_thresh", [("j < kk; ++j)", "j < 1; ++j)")]),
+    ("near_absolute_band", "int64_t oracle_near_ties", [("<= rel * fabs(t)", "<= rel")]),
+    ("near_one_sided", "int64_t oracle_near_ties", [("fabs(s64[k] - t)", "(s64[k] - t)")]),
+    ("near_band_around_max", "int64_t oracle_near_ties",
+     [("if (s32[i] < s32[last] || (s32[i] == s32[last] && i > last))", "if (s32[i] > s32[last])")]),
+    ("near_lowest_index_of_tie", "int64_t oracle_near_ties", [("&& i > last))", "&& i < last))")]),
+    ("near_centred_on_key", "int64_t oracle_near_ties", [("double t = s64[last];", "double t = (double)s32[last];")]),
     ("pv_prefix_off_by_block", "int64_t oracle_pv_prefix", [("qblock * (g + 1)", "qblock * (g + 2)")]),
     ("pv_mass_drops_last_query", "void oracle_pv_scores", [("for (int64_t i = 0; i < nq; ++i)\n            mass", "for (int64_t i = 0; i < nq - 1; ++i)\n            mass")]),
     ("pv_score_without_vnorm", "void oracle_pv_scores", [("double s = mass * sqrt(vv);", "double s = mass;")]),
