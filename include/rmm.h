@@ -27,7 +27,8 @@
  * Conventions shared by every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
  *     allocates and frees nothing; scratch memory comes from a caller-owned
- *     workspace sized by the *_workspace_bytes functions.
+ *     workspace sized by the *_workspace_bytes functions (except
+ *     rmm_select_gather_noalloc, whose scratch is a fixed per-GPU array).
  *   - Matrices are row-major with explicit leading dimensions in elements.
  *   - Every device pointer is 16-byte aligned, and every leading dimension is
  *     a multiple of 8 (bf16) or 4 (fp32) elements: rows start 16-byte aligned.
@@ -37,10 +38,13 @@
  *     Work is enqueued asynchronously; no entry point synchronises the host.
  *   - Return value: RMM_OK, or RMM_EINVAL (bad argument, detected on the host
  *     before anything is enqueued), RMM_EUNSUPPORTED (valid but outside what
- *     the kernels handle, also before anything is enqueued) or RMM_EHIP (the
- *     HIP runtime reported an error when enqueueing).
+ *     the kernels handle, also before anything is enqueued), RMM_EHIP (the
+ *     HIP runtime reported an error when enqueueing) or RMM_ESCRATCH (only
+ *     rmm_select_gather_noalloc: the call needs more than its fixed scratch).
  *   - Inputs are assumed finite.  Entry points are re-entrant and stateless;
- *     calls on different streams that share no output buffer may overlap.
+ *     calls on different streams that share no output buffer may overlap
+ *     (rmm_select_gather_noalloc excepted: its calls on one GPU share one
+ *     scratch array).
  */
 #ifndef RMM_H
 #define RMM_H
@@ -56,6 +60,10 @@ extern "C" {
 #define RMM_EINVAL (-1)
 #define RMM_EUNSUPPORTED (-2)
 #define RMM_EHIP (-3)
+#define RMM_ESCRATCH (-4)   /* rmm_select_gather_noalloc: the call needs more than its scratch */
+
+/* Bytes of the fixed per-GPU scratch of rmm_select_gather_noalloc. */
+#define RMM_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 #define RMM_F32 0
 #define RMM_BF16 1
@@ -152,6 +160,33 @@ int rmm_select_gather(const void *A, int dt, int64_t M, int64_t K, int64_t lda, 
                       const void *B, int64_t N, int64_t ldb, double r, int64_t group_rows,
                       int32_t *idx, int64_t ldidx, uint16_t *Apanel, int64_t ldp, float *scores,
                       float *thresh, double *bound, void *ws, size_t ws_bytes, void *stream);
+
+/* rmm_select_gather without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and errors as
+ * rmm_select_gather minus ws / ws_bytes; the scratch it needs (the G x K
+ * binary32 scores unless `scores` is given, plus K binary64 B norms when they
+ * are computed from B) lives in a fixed array of RMM_NOALLOC_SCRATCH_BYTES
+ * (8 MiB) in device memory, one per GPU, that the library holds until the
+ * process ends.  Nothing is allocated or freed by the call.
+ *   - The array is found on the device current at the call (the stream must
+ *     belong to it); its address is looked up on the first call on each
+ *     device and kept.
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap
+ *     on one GPU (different streams, or host threads) race and must be
+ *     serialised by the caller.  The array keeps the last call's contents;
+ *     nothing in it needs to start at zero.
+ *   - rmm_select_workspace_bytes(M, K, group_rows, scores != NULL,
+ *     bnorm == NULL && B != NULL) must not exceed RMM_NOALLOC_SCRATCH_BYTES
+ *     (e.g. G * K <= 2^21 with bnorm given): otherwise RMM_ESCRATCH, before
+ *     anything is enqueued.
+ * Errors: those of rmm_select_gather (argument errors are decided on the host
+ * before any HIP call), RMM_ESCRATCH, RMM_EHIP if the scratch address cannot
+ * be obtained. */
+int rmm_select_gather_noalloc(const void *A, int dt, int64_t M, int64_t K, int64_t lda,
+                              const double *bnorm, const void *B, int64_t N, int64_t ldb, double r,
+                              int64_t group_rows, int32_t *idx, int64_t ldidx, uint16_t *Apanel,
+                              int64_t ldp, float *scores, float *thresh, double *bound, void *stream);
 
 /* Workspace bytes rmm_gemm needs (currently 0 for every shape). */
 size_t rmm_gemm_workspace_bytes(int64_t M, int64_t N, int64_t kk, int64_t group_rows);

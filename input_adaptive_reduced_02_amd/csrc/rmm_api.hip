@@ -7,7 +7,9 @@
 #include "rmm_internal.h"
 #include "rmm_select.h"
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 using namespace rmm;
 
@@ -54,6 +56,7 @@ const char *rmm_strerror(int status)
     case RMM_EINVAL: return "invalid argument";
     case RMM_EUNSUPPORTED: return "unsupported shape or type";
     case RMM_EHIP: return "HIP runtime error";
+    case RMM_ESCRATCH: return "the call needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
     }
 }
@@ -79,13 +82,11 @@ size_t rmm_select_workspace_bytes(int64_t M, int64_t K, int64_t group_rows, int 
 
 namespace {
 
-// Validation, B norms and column scores shared by rmm_select and
-// rmm_select_gather; on RMM_OK `sc` holds the G x K scores on the stream and
-// `sh` the selection shape.
-int linear_scores(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm, const void *B,
-                  int64_t N, int64_t ldb, double r, int64_t group_rows, int32_t *idx, int64_t ldidx,
-                  float *scores, float *thresh, double *bound, void *ws, size_t ws_bytes, hipStream_t s,
-                  float *&sc, SelectShape &sh)
+// Argument check of rmm_select and rmm_select_gather (host only, nothing is
+// enqueued): RMM_OK, RMM_EINVAL or RMM_EUNSUPPORTED.
+int linear_check(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm, const void *B,
+                 int64_t N, int64_t ldb, double r, int64_t group_rows, const int32_t *idx, int64_t ldidx,
+                 const float *scores, const float *thresh, const double *bound, const void *ws, size_t ws_bytes)
 {
     if (M < 1 || K < 1 || group_rows < 1 || !ok_matrix(A, dt, K, lda)) return RMM_EINVAL;
     const int64_t kk = rmm_kk(r, K);
@@ -100,6 +101,22 @@ int linear_scores(const void *A, int dt, int64_t M, int64_t K, int64_t lda, cons
     const size_t need = rmm_select_workspace_bytes(M, K, group_rows, scores != nullptr, from_B);
     if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
     if (K > kSelectMaxK) return RMM_EUNSUPPORTED;
+    return RMM_OK;
+}
+
+// Validation, B norms and column scores shared by rmm_select and
+// rmm_select_gather; on RMM_OK `sc` holds the G x K scores on the stream and
+// `sh` the selection shape.
+int linear_scores(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm, const void *B,
+                  int64_t N, int64_t ldb, double r, int64_t group_rows, int32_t *idx, int64_t ldidx,
+                  float *scores, float *thresh, double *bound, void *ws, size_t ws_bytes, hipStream_t s,
+                  float *&sc, SelectShape &sh)
+{
+    if (int st = linear_check(A, dt, M, K, lda, bnorm, B, N, ldb, r, group_rows, idx, ldidx, scores, thresh,
+                              bound, ws, ws_bytes))
+        return st;
+    const int64_t kk = rmm_kk(r, K);
+    const bool from_B = !bnorm && B;
 
     const int64_t G = (M + group_rows - 1) / group_rows;
     char *w = (char *)ws;
@@ -480,3 +497,61 @@ int rmm_pv_select_scores(const float *scores, int64_t H, int64_t L, double r, in
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation variant
+// Scratch of rmm_select_gather_noalloc: a fixed array in device memory, one
+// copy per GPU the library runs on, held until the process ends.  Host code
+// never passes the array's own name to a kernel or a copy (in host code it is
+// a stand-in, not a device address): it passes the address
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[RMM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_ptr(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RMM_EHIP;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RMM_EHIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return RMM_OK;
+}
+
+}  // namespace
+
+extern "C" int rmm_select_gather_noalloc(const void *A, int dt, int64_t M, int64_t K, int64_t lda,
+                                         const double *bnorm, const void *B, int64_t N, int64_t ldb, double r,
+                                         int64_t group_rows, int32_t *idx, int64_t ldidx, uint16_t *Apanel,
+                                         int64_t ldp, float *scores, float *thresh, double *bound, void *stream)
+{
+    // every argument check of rmm_select_gather first, against a workspace of
+    // unlimited size (nothing is enqueued and no HIP call is made on failure)
+    const int64_t kk = rmm_kk(r, K);
+    if (kk < 1 || !ok_matrix(Apanel, RMM_BF16, pad_up(kk), ldp)) return RMM_EINVAL;
+    static const __attribute__((aligned(256))) unsigned char stand_in[16] = {};
+    if (int st = linear_check(A, dt, M, K, lda, bnorm, B, N, ldb, r, group_rows, idx, ldidx, scores, thresh,
+                              bound, stand_in, SIZE_MAX))
+        return st;
+    const size_t need = rmm_select_workspace_bytes(M, K, group_rows, scores != nullptr, !bnorm && B);
+    if (need > RMM_NOALLOC_SCRATCH_BYTES) return RMM_ESCRATCH;
+    void *ws = nullptr;
+    if (int st = scratch_ptr(&ws)) return st;
+    // the scores (and B norms computed on the fly) are written in full before
+    // they are read, so the contents a previous call left need no clearing
+    return rmm_select_gather(A, dt, M, K, lda, bnorm, B, N, ldb, r, group_rows, idx, ldidx, Apanel, ldp, scores,
+                             thresh, bound, ws, RMM_NOALLOC_SCRATCH_BYTES, stream);
+}

@@ -18,7 +18,8 @@ import torch
 # the library built in-tree; RMM_LIB selects another build of it
 LIB_PATH = os.environ.get("RMM_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "librmm.so")
 
-RMM_OK, RMM_EINVAL, RMM_EUNSUPPORTED, RMM_EHIP = 0, -1, -2, -3
+RMM_OK, RMM_EINVAL, RMM_EUNSUPPORTED, RMM_EHIP, RMM_ESCRATCH = 0, -1, -2, -3, -4
+RMM_NOALLOC_SCRATCH_BYTES = 8 << 20
 RMM_F32, RMM_BF16 = 0, 1
 KPAD = 64
 
@@ -66,6 +67,9 @@ def _declare(L):
     L.rmm_select_gather.argtypes = [_P, _I, _L, _L, _L, _P, _P, _L, _L, _Dbl, _L, _P, _L, _P, _L, _P, _P, _P,
                                     _P, _S, _P]
     L.rmm_gather.argtypes = [_P, _I, _L, _L, _L, _P, _L, _L, _L, _P, _L, _P, _L, _L, _P, _L, _P]
+    L.rmm_select_gather_noalloc.restype = _I
+    L.rmm_select_gather_noalloc.argtypes = [_P, _I, _L, _L, _L, _P, _P, _L, _L, _Dbl, _L, _P, _L, _P, _L, _P, _P,
+                                            _P, _P]
     L.rmm_gemm_workspace_bytes.restype = _S
     L.rmm_gemm_workspace_bytes.argtypes = [_L, _L, _L, _L]
     L.rmm_gemm.restype = _I
@@ -207,6 +211,21 @@ def rmm_select_gather(A, r, group_rows, bnorm=None, B=None, idx=None, Apanel=Non
         _ptr(A), _dt(A), M, K, _ld(A), _ptr(bnorm), _ptr(B) if from_B else None, N, ldb, float(r),
         group_rows, _ptr(idx), _ld(idx), _ptr(Apanel), _ld(Apanel), _ptr(scores), _ptr(thresh), _ptr(bound),
         _ptr(w), need, _stream(A)))
+    return idx, Apanel
+
+
+def rmm_select_gather_noalloc(A, r, group_rows, idx, Apanel, bnorm=None, B=None, scores=None, thresh=None,
+                              bound=None):
+    """rmm_select_gather with the library's fixed per-GPU scratch instead of a
+    workspace: the caller passes every output (idx [G, >= kk_pad] int32, Apanel
+    [M, >= kk_pad] bf16), so the call allocates nothing.  Returns (idx, Apanel)."""
+    M, K = A.shape
+    from_B = bnorm is None and B is not None
+    N, ldb = (B.shape[1], _ld(B)) if from_B else (0, 0)
+    _check("rmm_select_gather_noalloc", lib().rmm_select_gather_noalloc(
+        _ptr(A), _dt(A), M, K, _ld(A), _ptr(bnorm), _ptr(B) if from_B else None, N, ldb, float(r),
+        group_rows, _ptr(idx), _ld(idx), _ptr(Apanel), _ld(Apanel), _ptr(scores), _ptr(thresh), _ptr(bound),
+        _stream(A)))
     return idx, Apanel
 
 

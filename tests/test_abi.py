@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -153,6 +153,30 @@ def test_validation_rejects_bad_arguments():
     assert selg(ldidx=32) == EINVAL
     assert selg(wsb=ws_need - 1) == EINVAL
     assert selg(K=40000, lda=40000, ldidx=20032, ldp=20032, wsb=4 * 40000 * 4) == EUNSUP
+    # select_gather_noalloc: the select_gather arguments without the workspace;
+    # argument errors and a scratch overflow are decided before any HIP call
+    ESCRATCH = -4
+
+    def selg0(Ap=P2, ldp=64, **kw):
+        a = dict(good, **kw)
+        return L.rmm_select_gather_noalloc(a["A"], a["dt"], a["M"], a["K"], a["lda"], a["bn"], a["B"], a["N"],
+                                           a["ldb"], a["r"], a["gr"], a["idx"], a["ldidx"], Ap, ldp, a["sc"],
+                                           a["th"], a["bd"], None)
+    for bad_r in (0.0, 1.5, nan):
+        assert selg0(r=bad_r) == EINVAL, bad_r
+    assert selg0(Ap=None) == EINVAL
+    assert selg0(ldp=32) == EINVAL
+    assert selg0(A=MIS) == EINVAL
+    assert selg0(idx=None) == EINVAL
+    assert selg0(bn=None, B=P, N=8, ldb=4) == EINVAL
+    assert selg0(K=40000, lda=40000, ldidx=20032, ldp=20032) == EUNSUP
+    # 65 groups x 32768 binary32 scores = 8.5 MB > the 8 MiB scratch; 64 groups fit
+    big = dict(K=32768, lda=32768, ldidx=16384, gr=16)
+    assert selg0(M=16 * 65, ldp=16384, **big) == ESCRATCH
+    assert L.rmm_select_workspace_bytes(16 * 64, 32768, 16, 0, 0) <= 8 << 20
+    # norms computed from B take K binary64 more: 64 groups no longer fit
+    assert selg0(M=16 * 64, ldp=16384, bn=None, B=P, N=8, ldb=8, **big) == ESCRATCH
+    assert L.rmm_strerror(ESCRATCH).decode().startswith("the call needs more scratch")
     # gather(A, dt, M, K, lda, idx, ldidx, kk, gr, Ap, ldp, B, N, ldb, Bp, ldbp, stream)
     assert L.rmm_gather(P, BF, 64, 64, 64, P2, 64, 0, 64, P3, 64, None, 0, 0, None, 0, None) == EINVAL
     assert L.rmm_gather(P, BF, 64, 64, 64, P2, 64, 65, 64, P3, 128, None, 0, 0, None, 0, None) == EINVAL
