@@ -127,6 +127,25 @@ int rmm_select(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const d
                int32_t *idx, int64_t ldidx, float *scores, float *thresh, double *bound,
                void *ws, size_t ws_bytes, void *stream);
 
+/* The two halves of rmm_select as calls of their own, so a caller (or a
+ * benchmark) can run or time the score and the selection separately; their
+ * outputs are bit for bit those rmm_select forms.
+ * rmm_scores ("Estrategia de Selecao": the score of every slice):
+ *   scores[g][k] = binary32( ||A[rows_g, k]||_2 * b_k ), b_k as in rmm_select
+ *   (bnorm; else the row norms of B, computed now into the workspace; else 1)
+ *   scores  [G][K] binary32, device; ws rmm_select_workspace_bytes(M, K,
+ *   group_rows, 1, bnorm == NULL && B != NULL) bytes (0 unless norms come from B)
+ * rmm_select_scores (the top-kk selection of every group from given scores):
+ *   scores [G][ld_scores] binary32 (ld_scores >= K), kk = rmm_kk(r, K); idx,
+ *   thresh and bound exactly as rmm_select writes them (bound is the sum of
+ *   the dropped scores as given).  No workspace.
+ * Errors: as rmm_select. */
+int rmm_scores(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm,
+               const void *B, int64_t N, int64_t ldb, int64_t group_rows, float *scores, void *ws,
+               size_t ws_bytes, void *stream);
+int rmm_select_scores(const float *scores, int64_t G, int64_t K, int64_t ld_scores, double r,
+                      int32_t *idx, int64_t ldidx, float *thresh, double *bound, void *stream);
+
 /* Gather ("Mecanismo Central": the columns A[:, I] of the reduced product)
  * into a contiguous bf16 panel:
  *   Apanel[m][j] = bf16(A[m][idx[g*ldidx + j]])  for j < kk, g = m / group_rows

@@ -159,6 +159,45 @@ int rmm_select(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const d
     return hip_status(launch_select(sc, sh, idx, ldidx, thresh, bound, s));
 }
 
+int rmm_scores(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm, const void *B,
+               int64_t N, int64_t ldb, int64_t group_rows, float *scores, void *ws, size_t ws_bytes, void *stream)
+{
+    if (M < 1 || K < 1 || group_rows < 1 || !ok_matrix(A, dt, K, lda)) return RMM_EINVAL;
+    if (!scores || !aligned4(scores)) return RMM_EINVAL;
+    if (bnorm && !aligned8(bnorm)) return RMM_EINVAL;
+    const bool from_B = !bnorm && B;
+    if (from_B && !ok_matrix(B, dt, N, ldb)) return RMM_EINVAL;
+    const size_t need = rmm_select_workspace_bytes(M, K, group_rows, 1, from_B);
+    if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
+    hipStream_t s = as_stream(stream);
+    const double *bn = bnorm;
+    if (from_B) {
+        double *tmp = (double *)ws;
+        if (hipError_t e = launch_rownorms(B, dt, K, N, ldb, tmp, s)) return hip_status(e);
+        bn = tmp;
+    }
+    return hip_status(launch_colscore(A, dt, M, K, lda, bn, group_rows, scores, s));
+}
+
+int rmm_select_scores(const float *scores, int64_t G, int64_t K, int64_t ld_scores, double r, int32_t *idx,
+                      int64_t ldidx, float *thresh, double *bound, void *stream)
+{
+    if (G < 1 || K < 1 || ld_scores < K || !scores || !aligned4(scores)) return RMM_EINVAL;
+    const int64_t kk = rmm_kk(r, K);
+    if (kk < 1) return RMM_EINVAL;
+    if (!idx || !aligned16(idx) || ldidx < pad_up(kk) || ldidx % 4 != 0) return RMM_EINVAL;
+    if (thresh && !aligned4(thresh)) return RMM_EINVAL;
+    if (bound && !aligned8(bound)) return RMM_EINVAL;
+    if (K > kSelectMaxK) return RMM_EUNSUPPORTED;
+    SelectShape sh{};
+    sh.groups = G;
+    sh.K = K;
+    sh.lds = ld_scores;
+    sh.kk = kk;
+    sh.pv = 0;
+    return hip_status(launch_select(scores, sh, idx, ldidx, thresh, bound, as_stream(stream)));
+}
+
 int rmm_select_gather(const void *A, int dt, int64_t M, int64_t K, int64_t lda, const double *bnorm,
                       const void *B, int64_t N, int64_t ldb, double r, int64_t group_rows, int32_t *idx,
                       int64_t ldidx, uint16_t *Apanel, int64_t ldp, float *scores, float *thresh,

@@ -67,6 +67,10 @@ def _declare(L):
     L.rmm_select_gather.argtypes = [_P, _I, _L, _L, _L, _P, _P, _L, _L, _Dbl, _L, _P, _L, _P, _L, _P, _P, _P,
                                     _P, _S, _P]
     L.rmm_gather.argtypes = [_P, _I, _L, _L, _L, _P, _L, _L, _L, _P, _L, _P, _L, _L, _P, _L, _P]
+    L.rmm_scores.restype = _I
+    L.rmm_scores.argtypes = [_P, _I, _L, _L, _L, _P, _P, _L, _L, _L, _P, _P, _S, _P]
+    L.rmm_select_scores.restype = _I
+    L.rmm_select_scores.argtypes = [_P, _L, _L, _L, _Dbl, _P, _L, _P, _P, _P]
     L.rmm_select_gather_noalloc.restype = _I
     L.rmm_select_gather_noalloc.argtypes = [_P, _I, _L, _L, _L, _P, _P, _L, _L, _Dbl, _L, _P, _L, _P, _L, _P, _P,
                                             _P, _P]
@@ -212,6 +216,36 @@ def rmm_select_gather(A, r, group_rows, bnorm=None, B=None, idx=None, Apanel=Non
         group_rows, _ptr(idx), _ld(idx), _ptr(Apanel), _ld(Apanel), _ptr(scores), _ptr(thresh), _ptr(bound),
         _ptr(w), need, _stream(A)))
     return idx, Apanel
+
+
+def rmm_scores(A, group_rows, bnorm=None, B=None, scores=None, ws=None):
+    """Per-group slice scores [G, K] binary32 (the score half of rmm_select)."""
+    M, K = A.shape
+    G = -(-M // group_rows)
+    if scores is None:
+        scores = torch.empty((G, K), dtype=torch.float32, device=A.device)
+    from_B = bnorm is None and B is not None
+    need = rmm_select_workspace_bytes(M, K, group_rows, True, from_B)
+    w = _ws(need, A.device, ws)
+    N, ldb = (B.shape[1], _ld(B)) if from_B else (0, 0)
+    _check("rmm_scores", lib().rmm_scores(
+        _ptr(A), _dt(A), M, K, _ld(A), _ptr(bnorm), _ptr(B) if from_B else None, N, ldb, group_rows,
+        _ptr(scores), _ptr(w), need, _stream(A)))
+    return scores
+
+
+def rmm_select_scores(scores, r, idx=None, thresh=None, bound=None):
+    """Kept indices [G, kk_pad] from given scores [G, K] (the selection half of rmm_select)."""
+    G, K = scores.shape
+    kk = rmm_kk(r, K)
+    if kk < 1:
+        raise ValueError("r must lie in (0, 1]")
+    if idx is None:
+        idx = torch.empty((G, rmm_kk_pad(kk)), dtype=torch.int32, device=scores.device)
+    _check("rmm_select_scores", lib().rmm_select_scores(
+        _ptr(scores), G, K, _ld(scores), float(r), _ptr(idx), _ld(idx), _ptr(thresh), _ptr(bound),
+        _stream(scores)))
+    return idx
 
 
 def rmm_select_gather_noalloc(A, r, group_rows, idx, Apanel, bnorm=None, B=None, scores=None, thresh=None,

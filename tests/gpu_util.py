@@ -9,6 +9,9 @@ with S = sum_k |a_k| |b_k| over the kept slices, times 1.01 for the roundings of
 the bound itself.  On top of that, every output matrix must be within the
 relative Frobenius error 5e-3 of the oracle.
 """
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import torch
 
@@ -16,6 +19,36 @@ import oracle as O
 
 DEV = "cuda:0"
 FROB_TOL = 5e-3
+
+
+# host threads the oracle runs on (each call is single-threaded C; ctypes
+# releases the GIL, so calls on different rows run on different cores)
+ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def group_rows_sample(M, gr):
+    """Rows compared at full size: all of them for a single group, else the
+    first, the two middle and the last row of every group."""
+    if -(-M // gr) == 1:
+        return np.arange(M)
+    offs = (0, gr // 2 - 1, gr // 2, gr - 1)
+    return np.unique([min(M - 1, g * gr + o) for g in range(-(-M // gr)) for o in offs])
+
+
+def oracle_rows(A64, B64, idx, kk, gr, rows, A64abs=None, B64abs=None):
+    """(Y, S) of the oracle's reduced product for the given rows, every column:
+    Y the product, S the same sum over |a_k b_k| (the scale of the element
+    bound); one single-threaded oracle call per row, on a thread pool."""
+    A64abs = np.abs(A64) if A64abs is None else A64abs
+    B64abs = np.abs(B64) if B64abs is None else B64abs
+
+    def one(m):
+        return (O.reduced(A64, B64, idx, kk, gr, m0=m, m1=m + 1)[0],
+                O.reduced(A64abs, B64abs, idx, kk, gr, m0=m, m1=m + 1)[0])
+
+    with cf.ThreadPoolExecutor(ORACLE_THREADS) as ex:
+        out = list(ex.map(one, [int(m) for m in rows]))
+    return np.stack([y for y, _ in out]), np.stack([a for _, a in out])
 
 
 def log(*a):

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -153,6 +153,21 @@ def test_validation_rejects_bad_arguments():
     assert selg(ldidx=32) == EINVAL
     assert selg(wsb=ws_need - 1) == EINVAL
     assert selg(K=40000, lda=40000, ldidx=20032, ldp=20032, wsb=4 * 40000 * 4) == EUNSUP
+    # scores(A, dt, M, K, lda, bnorm, B, N, ldb, gr, scores, ws, wsb, stream)
+    assert L.rmm_scores(None, BF, 64, 64, 64, P3, None, 0, 0, 16, P2, None, 0, None) == EINVAL
+    assert L.rmm_scores(P, BF, 64, 64, 32, P3, None, 0, 0, 16, P2, None, 0, None) == EINVAL   # lda < K
+    assert L.rmm_scores(P, BF, 64, 64, 64, P3, None, 0, 0, 0, P2, None, 0, None) == EINVAL    # gr < 1
+    assert L.rmm_scores(P, BF, 64, 64, 64, P3, None, 0, 0, 16, None, None, 0, None) == EINVAL  # no scores
+    assert L.rmm_scores(P, BF, 64, 64, 64, None, P, 8, 8, 16, P2, None, 0, None) == EINVAL    # norms from B, no ws
+    # select_scores(scores, G, K, ld, r, idx, ldidx, thresh, bound, stream)
+    for bad_r in (0.0, 1.5, nan):
+        assert L.rmm_select_scores(P, 4, 64, 64, bad_r, P2, 64, None, None, None) == EINVAL, bad_r
+    assert L.rmm_select_scores(None, 4, 64, 64, 0.5, P2, 64, None, None, None) == EINVAL
+    assert L.rmm_select_scores(P, 4, 64, 32, 0.5, P2, 64, None, None, None) == EINVAL   # ld < K
+    assert L.rmm_select_scores(P, 4, 64, 64, 0.5, P2, 32, None, None, None) == EINVAL   # ldidx < kk_pad
+    assert L.rmm_select_scores(P, 4, 64, 64, 0.5, None, 64, None, None, None) == EINVAL
+    assert L.rmm_select_scores(P, 4, 64, 64, 0.5, P2, 64, MIS, None, None) == EINVAL
+    assert L.rmm_select_scores(P, 4, 40000, 40000, 0.5, P2, 20032, None, None, None) == EUNSUP
     # select_gather_noalloc: the select_gather arguments without the workspace;
     # argument errors and a scratch overflow are decided before any HIP call
     ESCRATCH = -4

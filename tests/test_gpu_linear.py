@@ -4,7 +4,7 @@ GEMM, and the r = 1 dense baseline) against the oracle, through the C ABI.
 Small cases span several tiles and ragged tails (short last group, N not a
 multiple of the tile, kk not a multiple of 8 or 64) and are compared element by
 element; the full workload sizes are compared on every group's scores and kept
-set and on sampled output rows.  Scores, B norms, kept sets and panels must be
+set and on four output rows of every group.  Scores, B norms, kept sets and panels must be
 bit-exact (both sides sum in binary64 in ascending order and round once to
 binary32); outputs within the bound documented in tests/gpu_util.py.
 """
@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import DEV, check_output, compare_sets, down, log, up_bf16, up_f32, widen
+from gpu_util import (DEV, check_output, compare_sets, down, group_rows_sample, log, oracle_rows, up_bf16,
+                      up_f32, widen)
 from input_adaptive_reduced_02_amd import rmm, synth
 
 pytestmark = pytest.mark.gpu
@@ -268,7 +269,9 @@ def _full(workload):
 @pytest.mark.parametrize("workload,r", FULL, ids=lambda x: str(x))
 def test_full_size(workload, r):
     """Full workload shape, in the launch configuration the benchmark times:
-    every group's scores and kept set exact; sampled rows element by element."""
+    every group's scores and kept set exact; the first, middle and last rows of
+    every group (every row of a single group) element by element over all N
+    columns."""
     c = _full(workload)
     M, K = c["A"].shape
     N = c["B"].shape[1]
@@ -276,9 +279,8 @@ def test_full_size(workload, r):
     tag = f"{workload} {M}x{K}x{N} r={r}"
     log(f"full {tag}")
     assert np.array_equal(down(c["bnorm"]), c["b_ref"])
-    rng = np.random.default_rng(11)
     G = -(-M // gr)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, G)]))
+    rows = group_rows_sample(M, gr)
     if r == 1.0:
         Y = rmm.linear(c["A"], c["B"], r, gr, bnorm=c["bnorm"])
         torch.cuda.synchronize()
@@ -289,9 +291,8 @@ def test_full_size(workload, r):
         sel, ig = check_selection(c, r, gr, c["bnorm"], idx, scores, thresh, bound, tag)
         kk = sel["kk"]
     Yg = widen(Y)
-    Yref = np.stack([O.reduced(c["A64"], c["B64"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
-    Sabs = np.stack([O.reduced(c["A64abs"], c["B64abs"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
-    check_output(Yg[rows], Yref, Sabs, kk, tag + f" ({len(rows)} rows)")
+    Yref, Sabs = oracle_rows(c["A64"], c["B64"], ig, kk, gr, rows, c["A64abs"], c["B64abs"])
+    check_output(Yg[rows], Yref, Sabs, kk, tag + f" ({len(rows)} rows: every group)")
 
 
 @pytest.mark.parametrize("case", [("attn_proj", 4096, 1000, 8, 8, 0.3), ("decode", 2048, 3000, 8, 4, 0.5),
@@ -325,7 +326,8 @@ def test_select_many_groups(case):
 def test_full_size_activation_only(workload, r):
     """The pages' activation-only rule (score = ||A[rows_g, k]||_2, no B norms)
     at full size: every group's scores and kept set against the oracle's
-    activation-only selection, sampled output rows element by element."""
+    activation-only selection, four output rows of every group (every row of a
+    single group) element by element."""
     c = _full(workload)
     M, K = c["A"].shape
     N = c["B"].shape[1]
@@ -346,10 +348,9 @@ def test_full_size_activation_only(workload, r):
     Ap, _ = rmm.rmm_gather(c["A"], idx, kk, gr)
     Y = rmm.rmm_gemm(Ap, c["B"], idx, kk, gr)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(12).integers(0, M, G)]))
-    Yref = np.stack([O.reduced(c["A64"], c["B64"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
-    Sabs = np.stack([O.reduced(c["A64abs"], c["B64abs"], ig, kk, gr, m0=m, m1=m + 1)[0] for m in rows])
-    check_output(widen(Y)[rows], Yref, Sabs, kk, tag + f" ({len(rows)} rows)")
+    rows = group_rows_sample(M, gr)
+    Yref, Sabs = oracle_rows(c["A64"], c["B64"], ig, kk, gr, rows, c["A64abs"], c["B64abs"])
+    check_output(widen(Y)[rows], Yref, Sabs, kk, tag + f" ({len(rows)} rows: every group)")
 
 
 # ---------------------------------------------------------------- select + gather in one call
@@ -421,3 +422,47 @@ def test_select_gather_equals_select_then_gather(case):
         for m in np.unique(np.linspace(0, MM - 1, 17).astype(int)):
             assert np.array_equal(pan[m, :kk], A_bits[m, ig[m // gr, :kk]]), f"{tag}: panel row {m}"
             assert np.all(pan[m, kk:] == 0), f"{tag}: panel padding row {m}"
+
+
+# ---------------------------------------------------------------- score and selection as separate calls
+@pytest.mark.parametrize("case", [("attn_proj", 300, 1000, 64, 128, 0.37, "cache"),
+                                  ("mlp_down", 256, 14336, 64, 128, 0.5, "from_B"),
+                                  ("decode", 64, 8192, 64, 64, 0.3, "none"),
+                                  ("attn_proj", 4096, 1000, 8, 8, 0.3, "cache")],
+                         ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-g{c[4]}-r{c[5]}-{c[6]}")
+def test_scores_then_select_scores(case):
+    """rmm_scores followed by rmm_select_scores gives, bit for bit, the scores,
+    kept indices (with padding), thresholds and bounds of rmm_select, and the
+    scores and kept sets of the oracle: B norms cached, computed from B, and
+    absent (the activation-only rule); one group per thread block and the
+    one-wave-per-group selection (512 groups)."""
+    workload, M, K, N, gr, r, norms = case
+    tag = f"scores+select {workload} {M}x{K} gr={gr} r={r} {norms}"
+    log(f"case {tag}")
+    c = make_case(workload, M, K, N, seed=27)
+    bnorm = rmm.rmm_rownorms(c["B"]) if norms == "cache" else None
+    B = c["B"] if norms == "from_B" else None
+    kk = rmm.rmm_kk(r, K)
+    G = -(-M // gr)
+    outs = []
+    for split in (False, True):
+        sc = torch.full((G, K), -1.0, dtype=torch.float32, device=DEV)
+        th = torch.full((G,), -1.0, dtype=torch.float32, device=DEV)
+        bd = torch.full((G,), -1.0, dtype=torch.float64, device=DEV)
+        ix = torch.full((G, rmm.rmm_kk_pad(kk)), -7, dtype=torch.int32, device=DEV)
+        if split:
+            rmm.rmm_scores(c["A"], gr, bnorm=bnorm, B=B, scores=sc)
+            rmm.rmm_select_scores(sc, r, idx=ix, thresh=th, bound=bd)
+        else:
+            rmm.rmm_select(c["A"], r, gr, bnorm=bnorm, B=B, idx=ix, scores=sc, thresh=th, bound=bd)
+        torch.cuda.synchronize()
+        outs.append((sc, ix, th, bd))
+    for name, a, b in zip(("scores", "idx", "thresh", "bound"), *outs):
+        assert torch.equal(a, b), f"{tag}: {name} differs from rmm_select"
+    b64 = None if norms == "none" else O.rownorms(c["B64"])
+    sel = O.select(c["A64"], r, gr, b64)
+    assert np.array_equal(down(outs[1][0]), sel["s32"]), f"{tag}: scores differ from the oracle"
+    ig = down(outs[1][1])
+    for g in range(G):
+        compare_sets(ig[g], sel, g, kk, tag)
+    assert np.array_equal(down(outs[1][2]), sel["thresh"]), f"{tag}: thresholds differ from the oracle"
