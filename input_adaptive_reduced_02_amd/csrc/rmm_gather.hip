@@ -61,60 +61,106 @@ k_gather_a(const void *__restrict__ Av, int64_t M, int64_t lda, const int32_t *_
 }
 
 constexpr int kGatherLds = 32768;   // longest A row (bytes) staged in LDS
+constexpr int kGatherIdx = 4;       // panel chunks per thread whose indices are loaded ahead
 
-// One workgroup per `rpw` consecutive rows: the rows go to LDS (16-byte
-// chunks, the ragged end of a row element by element), then thread t writes
-// panel chunks t, t + 256, ... of every row.
+// DMA: every lane copies 16 bytes from its global address to LDS[m0 + 16*lane]
+__device__ __forceinline__ void gather_dma16(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+// One workgroup per `rpw` consecutive rows.  The rows go to LDS by DMA in
+// 1 KiB blocks, every block of the workgroup in flight at once (wave w issues
+// blocks w, w + 4, ...; lanes past a row's last 16-byte chunk re-read the
+// row's start into staging space no pick reads).  While they land, every
+// thread loads the kept indices of its first panel chunks into registers.
+// Then thread t writes panel chunks t, t + 256, ... of every row, picking the
+// 8 kept elements of a chunk out of LDS.  A row's chunks all lie inside its
+// leading dimension (lda * es is a multiple of 16 and K <= lda).
 template <int DT>
 __global__ void __launch_bounds__(256)
 k_gather_rows(const void *__restrict__ Av, int64_t M, int64_t K, int64_t lda, const int32_t *__restrict__ idx,
               int64_t ldidx, int64_t kk, int64_t gr, uint16_t *__restrict__ Ap, int64_t ldp, int rpw,
               int row_bytes)
 {
-    extern __shared__ __attribute__((aligned(16))) unsigned char stage[];
+    extern __shared__ __attribute__((aligned(1024))) unsigned char stage[];
     constexpr int ES = DT == 1 ? 2 : 4;
     const int64_t m0 = (int64_t)blockIdx.x * rpw;
     const int nrow = (int)((M - m0 < rpw) ? (M - m0) : rpw);
-    const int full = (int)(K * ES / 16);          // whole 16-byte chunks in a row
-    const int tid = threadIdx.x;
-    for (int r = 0; r < nrow; ++r) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int chunks = (int)((K * ES + 15) / 16);   // 16-byte chunks of a row holding its K elements
+    const int blocks = (chunks + 63) / 64;          // 1 KiB DMA blocks per row
+    const uint32_t st0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)stage;
+    for (int b = wave; b < nrow * blocks; b += 4) {
+        const int r = b / blocks, c = (b % blocks) * 64 + lane;
         const unsigned char *src = (const unsigned char *)Av + (m0 + r) * lda * ES;
-        unsigned char *dst = stage + r * row_bytes;
-        for (int c = tid; c < full; c += 256) *(uint4 *)(dst + 16 * c) = *(const uint4 *)(src + 16 * c);
-        for (int64_t e = (int64_t)full * 16 / ES + tid; e < K; e += 256) {
-            if (DT == 1) ((uint16_t *)dst)[e] = ((const uint16_t *)src)[e];
-            else ((float *)dst)[e] = ((const float *)src)[e];
+        gather_dma16(c < chunks ? src + 16 * c : src, st0 + r * row_bytes + (b % blocks) * 1024);
+    }
+    // indices of this thread's first chunks of the first row's group (a
+    // workgroup's rows may span two groups; the others load theirs below)
+    const int64_t cpr = pad_up(kk) / 8;
+    const int32_t *I0 = idx + (m0 / gr) * ldidx;
+    int4 ia[kGatherIdx], ib[kGatherIdx];
+#pragma unroll
+    for (int q = 0; q < kGatherIdx; ++q) {
+        const int64_t j0 = (int64_t)(tid + 256 * q) * 8;
+        ia[q] = ib[q] = int4{0, 0, 0, 0};
+        if (j0 + 8 <= kk) {
+            ia[q] = *(const int4 *)(I0 + j0);
+            ib[q] = *(const int4 *)(I0 + j0 + 4);
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int64_t cpr = pad_up(kk) / 8;
+    // panel chunk j0/8 of staged row `row`, its indices given (full chunks) or
+    // read from I (the chunk that reaches kk)
+    auto pick = [&](const unsigned char *row, const int32_t *I, int64_t j0, int4 i0, int4 i1, uint16_t *out) {
+        uint32_t h[8];
+        if (j0 + 8 <= kk) {
+            const int32_t ks[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                h[e] = DT == 1 ? ((const uint16_t *)row)[ks[e]] : f32_to_bf16(((const float *)row)[ks[e]]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                h[e] = 0;
+                if (j0 + e < kk) {
+                    const int32_t k = I[j0 + e];
+                    h[e] = DT == 1 ? ((const uint16_t *)row)[k] : f32_to_bf16(((const float *)row)[k]);
+                }
+            }
+        }
+        // streaming store: the panel is read next by the GEMM on other CUs
+        const u32x4 o = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        __builtin_nontemporal_store(o, (u32x4 *)(out + j0));
+    };
     for (int r = 0; r < nrow; ++r) {
         const int64_t m = m0 + r;
         const int32_t *I = idx + (m / gr) * ldidx;
+        const bool same = (m / gr) == (m0 / gr);
         const unsigned char *row = stage + r * row_bytes;
         uint16_t *out = Ap + m * ldp;
-        for (int64_t c = tid; c < cpr; c += 256) {
-            const int64_t j0 = c * 8;
-            uint32_t h[8];
-            if (j0 + 8 <= kk) {
-                const int4 i0 = *(const int4 *)(I + j0);
-                const int4 i1 = *(const int4 *)(I + j0 + 4);
-                const int32_t ks[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    h[e] = DT == 1 ? ((const uint16_t *)row)[ks[e]] : f32_to_bf16(((const float *)row)[ks[e]]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    h[e] = 0;
-                    if (j0 + e < kk) {
-                        const int32_t k = I[j0 + e];
-                        h[e] = DT == 1 ? ((const uint16_t *)row)[k] : f32_to_bf16(((const float *)row)[k]);
-                    }
-                }
+        for (int q = 0; q < kGatherIdx; ++q) {
+            const int64_t j0 = (int64_t)(tid + 256 * q) * 8;
+            if (j0 >= cpr * 8) break;
+            int4 i0 = ia[q], i1 = ib[q];
+            if (!same && j0 + 8 <= kk) {
+                i0 = *(const int4 *)(I + j0);
+                i1 = *(const int4 *)(I + j0 + 4);
             }
-            *(uint4 *)(out + j0) =
-                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            pick(row, I, j0, i0, i1, out);
+        }
+        for (int64_t c = tid + 256 * kGatherIdx; c < cpr; c += 256) {
+            const int64_t j0 = c * 8;
+            int4 i0 = {0, 0, 0, 0}, i1 = {0, 0, 0, 0};
+            if (j0 + 8 <= kk) {
+                i0 = *(const int4 *)(I + j0);
+                i1 = *(const int4 *)(I + j0 + 4);
+            }
+            pick(row, I, j0, i0, i1, out);
         }
     }
 }
@@ -151,7 +197,8 @@ hipError_t launch_gather(const void *A, int dt, int64_t M, int64_t K, int64_t ld
 {
     const int64_t kpad = pad_up(kk);
     const int64_t cpr = kpad / 8;
-    const int64_t row_bytes = (K * (dt == 1 ? 2 : 4) + 15) / 16 * 16;
+    // staged row size: whole 1 KiB DMA blocks
+    const int64_t row_bytes = (K * (dt == 1 ? 2 : 4) + 1023) / 1024 * 1024;
     if (row_bytes <= kGatherLds) {
         // rows per workgroup: about 8 KiB of rows, so that many small
         // workgroups overlap one another's load and write phases on a CU
