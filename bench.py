@@ -253,9 +253,18 @@ class Linear:
         return brow + 2.0 * self.M * kk + yb * self.M * self.N
 
     bound = property(lambda self: "hbm" if self.name in ("decode", "decode_q8") else "mfma")
-    # the kernel the reduced GEMM runs on (groups of at most 64 rows: the decode kernel)
-    kernel = property(lambda self: "rmm::k_gemm_q8" if self.q8 else
-                      ("rmm::k_gemm_sk" if self.gr <= 64 else "rmm::k_gemm_dl"))
+
+    @property
+    def kernel(self):
+        """The kernel the reduced GEMM runs on: groups of at most 64 rows the
+        decode kernel; prefill shapes with at least 512 tiles of 128 x 256 and
+        bf16 output two workgroups per CU, other prefill shapes eight waves."""
+        if self.q8:
+            return "rmm::k_gemm_q8"
+        if self.gr <= 64:
+            return "rmm::k_gemm_sk"
+        tiles = self.G * -(-min(self.gr, self.M) // 128) * -(-self.N // 256)
+        return "rmm::k_gemm_wt" if tiles >= 512 and not self.f32 else "rmm::k_gemm_dl"
 
     def cpu_baseline(self, r, groups):
         """The oracle (single-threaded fp64 C) on `groups` row groups at ratio r:
@@ -544,7 +553,7 @@ def step_time(torch, stages, steps, warmup):
 # ------------------------------------------------------------------ HBM traffic
 # sources of the kernel the roofline is taken on, per workload family
 GEMM_SOURCES = {
-    "linear": ["rmm_gemm.hip", "rmm_gemm_dl.h", "rmm_gemm_sk.h", "rmm_tile.h", "rmm_internal.h"],
+    "linear": ["rmm_gemm.hip", "rmm_gemm_dl.h", "rmm_gemm_sk.h", "rmm_gemm_wt.h", "rmm_tile.h", "rmm_internal.h"],
     "pv": ["rmm_pv.hip", "rmm_tile.h", "rmm_internal.h"],
     "q8": ["rmm_q8.hip", "rmm_gemm_dl.h", "rmm_tile.h", "rmm_internal.h"],
     "attn": ["rmm_attn.hip", "rmm_tile.h", "rmm_internal.h"],

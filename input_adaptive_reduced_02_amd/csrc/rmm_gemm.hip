@@ -18,12 +18,17 @@
 // tile strip needs are fetched into that XCD's L2 once and reused by every
 // group.
 //
-// Two shapes are instantiated:
-//   prefill  TM=128 TN=256 BK=64  waves 2x2 of 64x128   (group_rows >= 128)
-//   narrow   TM=64  TN=64  BK=256 waves 2x2 of 32x32    (<= 64 rows per group,
-//            e.g. decode: many N tiles stream the kept rows of a wide weight)
+// Kernels, by shape:
+//   k_gemm_wt  128 x 256 tiles, 4 waves of 128 x 64, two workgroups per CU
+//              (groups of more than 64 rows, at least 512 tiles, bf16 output)
+//   k_gemm_dl  128 x 256 tiles, 8 waves of 64 x 64 (other prefill shapes)
+//   k_gemm_sk  64 x 128 tiles streaming the kept rows (<= 64 rows per group,
+//              e.g. decode: many N tiles over the kept rows of a wide weight)
+//   k_gemm     register-staged fallback (leading dimensions the DMA
+//              pipelines do not cover)
 #include "rmm_gemm_dl.h"
 #include "rmm_gemm_sk.h"
+#include "rmm_gemm_wt.h"
 
 #ifndef RMM_DL_WAVES
 #define RMM_DL_WAVES 8
@@ -189,12 +194,35 @@ static hipError_t launch_shape(const uint16_t *A, int64_t lda, const uint16_t *B
     return hipGetLastError();
 }
 
+// tiles from which the two-per-CU kernel runs: two per CU of the 256 CUs of an
+// MI355X (with fewer, a CU holds one workgroup and k_gemm_dl is faster)
+constexpr int64_t kWtMinTiles = 512;
+
 hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                        const int32_t *idx, int64_t ldidx, int64_t M, int64_t N, int64_t kk,
                        int64_t group_rows, void *Y, int ydt, int64_t ldy, hipStream_t s)
 {
     const int64_t rows = group_rows < M ? group_rows : M;
     const int64_t kslab = (kk + 63) / 64 * 64;
+    // two 128 x 256 workgroups per CU when there are at least two tiles per
+    // CU (bf16 output; A byte offsets fit 32 bits)
+    if (rows > 64 && lda >= kslab && (!idx || ldidx >= kslab) && ydt == 1 && M * lda * 2 < (int64_t(1) << 32)) {
+        using S = WtShape<256, 32, 3>;
+        const int64_t G = (M + group_rows - 1) / group_rows;
+        const int tpg = (int)((rows + S::TM - 1) / S::TM);
+        const int m_tiles = (int)(G * tpg);
+        const int n_tiles = (int)((N + S::TN - 1) / S::TN);
+        if ((int64_t)m_tiles * n_tiles >= kWtMinTiles) {
+            const int per = (m_tiles * n_tiles + 7) / 8;
+            if (idx)
+                hipLaunchKernelGGL((k_gemm_wt<256, 32, 3, true>), dim3((unsigned)(8 * per)), dim3(256), 0, s, A, lda,
+                                   B, ldb, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy, tpg, m_tiles, n_tiles);
+            else
+                hipLaunchKernelGGL((k_gemm_wt<256, 32, 3, false>), dim3((unsigned)(8 * per)), dim3(256), 0, s, A,
+                                   lda, B, ldb, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy, tpg, m_tiles, n_tiles);
+            return hipGetLastError();
+        }
+    }
     // DMA pipeline: every A row and index row must be readable up to the slab end
     if (rows > 64 && lda >= kslab && (!idx || ldidx >= kslab)) {
         constexpr int NW = RMM_DL_WAVES, WMS = RMM_DL_WM;

@@ -466,3 +466,42 @@ def test_scores_then_select_scores(case):
     for g in range(G):
         compare_sets(ig[g], sel, g, kk, tag)
     assert np.array_equal(down(outs[1][2]), sel["thresh"]), f"{tag}: thresholds differ from the oracle"
+
+
+# ---------------------------------------------------------------- two workgroups per CU
+WT = [
+    # (M, K, N, group_rows, r): at least 512 tiles of 128 x 256, so bf16
+    # outputs take the two-workgroups-per-CU kernel
+    (4046, 1000, 4104, 128, 0.37),   # 32 groups, the last of 78 rows; N tail of 8; kk = 370
+    (4046, 1000, 4104, 128, 1.0),    # the dense product, A and B in place
+    (2048, 520, 8192, 256, 0.5),     # two row tiles per group; kk = 260 (ragged last slab)
+]
+
+
+@pytest.mark.parametrize("case", WT, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}-g{c[3]}-r{c[4]}")
+def test_two_per_cu_gemm(case):
+    """The prefill shapes with at least two tiles per CU: every output element
+    against the oracle, and the bf16 output equal to the round-to-nearest-even
+    bf16 of the binary32 output (which runs the eight-wave kernel, with the
+    same accumulation order)."""
+    M, K, N, gr, r = case
+    tag = f"two-per-CU {M}x{K}x{N} gr={gr} r={r}"
+    log(f"case {tag}")
+    G = -(-M // gr)
+    assert G * -(-min(gr, M) // 128) * -(-N // 256) >= 512
+    c = make_case("mlp_down", M, K, N, seed=33)
+    bnorm = rmm.rmm_rownorms(c["B"])
+    if r < 1.0:
+        idx, scores, thresh, bound, Ap, Y = run_chain(c, r, gr, bnorm)
+        sel, ig = check_selection(c, r, gr, bnorm, idx, scores, thresh, bound, tag)
+        kk = sel["kk"]
+        Y32 = rmm.rmm_gemm(Ap, c["B"], idx, kk, gr, ydt=torch.float32)
+    else:
+        kk = K
+        Y = rmm.rmm_gemm(c["A"], c["B"], None, K, gr)
+        Y32 = rmm.rmm_gemm(c["A"], c["B"], None, K, gr, ydt=torch.float32)
+        ig = np.arange(K, dtype=np.int32)[None, :].repeat(G, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(Y), synth.f32_to_bf16_bits(down(Y32))), f"{tag}: bf16 output is not RNE(fp32 output)"
+    Yref, Sabs = oracle_rows(c["A64"], c["B64"], ig, kk, gr, np.arange(M))
+    check_output(widen(Y), Yref, Sabs, kk, tag)
