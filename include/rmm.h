@@ -312,10 +312,11 @@ size_t rmm_gemm_q8_workspace_bytes(int64_t M, int64_t N, int64_t kk, int64_t gro
  * and a code is exact in fp32; the sum is accumulated in fp32 in a fixed
  * order (deterministic), and the scale multiplies it once; Y as rmm_gemm.
  * ws: rmm_gemm_q8_workspace_bytes(...) bytes, 16-byte aligned, ZERO-FILLED
- * before its first use with this shape; each call leaves it ready for the
- * next (its counters stay even), so a zero-filled workspace can be reused,
- * also by launches replayed from a HIP graph.  Calls that share a workspace
- * must not overlap.  Errors: RMM_EINVAL for bad pointers/sizes/workspace. */
+ * before its first use; each completed call leaves every arrival counter at
+ * zero again, so a zero-filled workspace can be reused by later calls of any
+ * shape that fits it, also by launches replayed from a HIP graph.  Calls that
+ * share a workspace must not overlap.  Errors: RMM_EINVAL for bad
+ * pointers/sizes/workspace. */
 int rmm_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq, const float *scale,
                 const int32_t *idx, int64_t ldidx, int64_t M, int64_t N, int64_t kk, int64_t group_rows,
                 void *Y, int ydt, int64_t ldy, void *ws, size_t ws_bytes, void *stream);

@@ -300,7 +300,7 @@ int rmm_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq, c
     const size_t need = gemm_q8_workspace_bytes(M, N, group_rows);
     if (need > ws_bytes || (need && (!ws || !aligned16(ws)))) return RMM_EINVAL;
     return hip_status(launch_gemm_q8(A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy,
-                                     ws, as_stream(stream)));
+                                     ws, ws_bytes, as_stream(stream)));
 }
 
 size_t rmm_attn_pv_workspace_bytes(int64_t H, int64_t L, int64_t D, double r, int64_t qblock,

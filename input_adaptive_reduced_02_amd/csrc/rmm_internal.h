@@ -104,7 +104,8 @@ hipError_t launch_rownorms_q8(const int8_t *q, int64_t ldq, const float *scale, 
 size_t gemm_q8_workspace_bytes(int64_t M, int64_t N, int64_t group_rows);
 hipError_t launch_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq,
                           const float *scale, const int32_t *idx, int64_t ldidx, int64_t M, int64_t N,
-                          int64_t kk, int64_t group_rows, void *Y, int ydt, int64_t ldy, void *ws, hipStream_t s);
+                          int64_t kk, int64_t group_rows, void *Y, int ydt, int64_t ldy, void *ws, size_t ws_bytes,
+                          hipStream_t s);
 hipError_t launch_pv_vnorm(const uint16_t *V, int64_t H, int64_t L, int64_t D, double *vnorm, hipStream_t s);
 hipError_t launch_qk_score(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int causal, int use_k,
                            double *ksum, float *scores, hipStream_t s);

@@ -432,13 +432,20 @@ k_gemm_q8(const uint16_t *__restrict__ A, int64_t lda, const int8_t *__restrict_
     // memory (thread-major: element e of thread x at e * threads + x, so
     // every store and load of a wave is one 256-byte run).  Each part stores
     // its sum with agent-coherent stores, waits for them to complete, then
-    // adds 1 to the tile's arrival counter; the part that finds the counter
-    // odd arrives second, reads the other sum with agent-coherent loads and
-    // adds the two in part order (the first part simply ends).  Only these
-    // words are made coherent -- no cache-wide write-back or invalidation.
-    // Every call adds 2 to each counter, so counters that start even (a
-    // zero-filled workspace) stay even from call to call, also when the
-    // launch is replayed from a graph.
+    // adds 1 to the tile's arrival counter; the part that finds 1 there
+    // arrives second, sets the counter back to 0, reads the other sum with
+    // agent-coherent loads and adds the two in part order (the first part
+    // simply ends).  Every counter is thus 0 after any completed call, so a
+    // workspace zero-filled once serves later calls of any shape, also
+    // launches replayed from a graph.
+    // Ordering: the partial sums are relaxed atomic stores and loads at agent
+    // scope (global_store/load with sc1, performed at the device-coherent
+    // level, not in an XCD's own L2), and s_waitcnt vmcnt(0) before the
+    // counter update waits for every one of them to be acknowledged; the
+    // second part issues its loads only after its counter update returned.
+    // Release/acquire at agent scope would add a write-back and an
+    // invalidation of the whole L2 around every handoff (measured 2.2x slower
+    // for the kernel), for words that already bypass it.
     if (ksplit == 2) {
         float *mine_ws = part_ws + ((int64_t)tile * 2 + kpart) * (TM * TN);
 #pragma unroll
@@ -453,7 +460,9 @@ k_gemm_q8(const uint16_t *__restrict__ A, int64_t lda, const int8_t *__restrict_
         if (threadIdx.x == 0) {
             const unsigned int old =
                 __hip_atomic_fetch_add(arrivals + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            second = (int)(old & 1u);
+            second = old == 1u;
+            if (second)   // both parts have arrived: nothing else touches this counter in this call
+                __hip_atomic_store(arrivals + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
         if (!second) return;
@@ -549,18 +558,27 @@ int q8_ksplit(int64_t M, int64_t N, int64_t group_rows)
     return tiles <= 128 ? 2 : 1;
 }
 
+// Workspace of a split call: the tiles' 4-byte arrival counters at its start
+// (256-byte aligned block), the two fp32 partial tiles per tile at its end.
+// With the counters at a fixed place and the partials right-aligned, the
+// counters of any shape that fits a workspace never lie where an earlier
+// call of another shape left partial sums.
+static size_t q8_counter_bytes(int64_t tiles) { return ((size_t)tiles * 4 + 255) / 256 * 256; }
+static size_t q8_partial_bytes(int64_t tiles) { return (size_t)tiles * 2 * Q8Shape::TM * Q8Shape::TN * sizeof(float); }
+
 size_t gemm_q8_workspace_bytes(int64_t M, int64_t N, int64_t group_rows)
 {
     using S = Q8Shape;
     if (q8_ksplit(M, N, group_rows) == 1) return 0;
     const int64_t G = (M + group_rows - 1) / group_rows;
     const int64_t tiles = G * ((group_rows + S::TM - 1) / S::TM) * ((N + S::TN - 1) / S::TN);
-    return (size_t)tiles * 2 * S::TM * S::TN * sizeof(float) + (size_t)tiles * 4;
+    return q8_counter_bytes(tiles) + q8_partial_bytes(tiles);
 }
 
 hipError_t launch_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq,
                           const float *scale, const int32_t *idx, int64_t ldidx, int64_t M, int64_t N,
-                          int64_t kk, int64_t group_rows, void *Y, int ydt, int64_t ldy, void *ws, hipStream_t s)
+                          int64_t kk, int64_t group_rows, void *Y, int ydt, int64_t ldy, void *ws, size_t ws_bytes,
+                          hipStream_t s)
 {
     using S = Q8Shape;
     const int64_t G = (M + group_rows - 1) / group_rows;
@@ -569,9 +587,13 @@ hipError_t launch_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int6
     const int n_tiles = (int)((N + S::TN - 1) / S::TN);
     const int ksplit = q8_ksplit(M, N, group_rows);
     const int total = m_tiles * n_tiles * ksplit;
-    float *part_ws = (float *)ws;
-    unsigned int *arrivals =
-        ksplit == 2 ? (unsigned int *)((char *)ws + (size_t)m_tiles * n_tiles * 2 * S::TM * S::TN * 4) : nullptr;
+    float *part_ws = nullptr;
+    unsigned int *arrivals = nullptr;
+    if (ksplit == 2) {   // ws_bytes >= q8_counter_bytes + q8_partial_bytes (checked by the caller)
+        arrivals = (unsigned int *)ws;
+        const size_t off = (ws_bytes - q8_partial_bytes((int64_t)m_tiles * n_tiles)) / 256 * 256;
+        part_ws = (float *)((char *)ws + off);
+    }
     const dim3 grid((unsigned)(8 * ((total + 7) / 8))), block(64 * S::NW);
     if (idx)
         hipLaunchKernelGGL(k_gemm_q8<true>, grid, block, 0, s, A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk,

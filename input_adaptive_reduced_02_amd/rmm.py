@@ -428,7 +428,8 @@ def rmm_gemm_q8(A, Bq, scale, idx, kk, group_rows, Y=None, ydt=torch.bfloat16, M
     w = _ws(need, A.device, ws)
     _check("rmm_gemm_q8", lib().rmm_gemm_q8(
         _ptr(A), _ld(A), _ptr(Bq), _ld(Bq), _ptr(scale), _ptr(idx), _ld(idx) if idx is not None else 0, M, N,
-        kk, group_rows, _ptr(Y), _dt(Y), _ld(Y), _ptr(w), need, _stream(A)))
+        kk, group_rows, _ptr(Y), _dt(Y), _ld(Y), _ptr(w), 0 if w is None else w.numel() * w.element_size(),
+        _stream(A)))
     return Y
 
 

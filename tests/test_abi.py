@@ -241,7 +241,7 @@ def test_validation_rejects_bad_arguments():
     assert L.rmm_gemm_q8(P, 64, P2, 40, P3, None, 0, 64, 32, 64, 64, P3, BF, 32, P3, W, None) == EINVAL    # ldq % 16
     assert L.rmm_gemm_q8(P, 64, P2, 32, P3, None, 0, 64, 32, 64, 64, P3, 5, 32, P3, W, None) == EINVAL     # ydt
     need = L.rmm_gemm_q8_workspace_bytes(64, 28672, 4096, 64)
-    assert need == 112 * 2 * 64 * 256 * 4 + 112 * 4
+    assert need == 112 * 2 * 64 * 256 * 4 + 512   # partial tiles + a 256-byte-aligned block of 112 counters
     assert L.rmm_gemm_q8_workspace_bytes(2048, 4096, 4096, 128) == 0            # 512 tiles: no split
     assert L.rmm_gemm_q8(P, 64, P2, 32, P3, None, 0, 64, 32, 64, 64, P3, BF, 32, P3, 16, None) == EINVAL   # short ws
     # qk_select(Q, K, H, L, D, r, qblock, causal, use_k, idx, ldidx, scores, ws, wsb, stream)

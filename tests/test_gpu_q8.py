@@ -242,3 +242,32 @@ def test_workspace_reuse_and_graph_replay():
         step()   # eager work between replays
         torch.cuda.synchronize()
         assert np.array_equal(down(Y), ref[0.5])
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace, zero-filled once and sized for the largest shape, serves
+    calls with different tile counts in any order (the arrival counters sit at
+    the start of the workspace and are back at zero after every call, the
+    partial sums at its end): each result equals the one from a fresh
+    zero-filled workspace."""
+    M, K, gr = 64, 1024, 64
+    d = synth.linear_inputs("decode", M, K, 4096, seed=12)
+    A = up_bf16(d["A"])
+    shapes = [4096, 2048, 4096, 1024, 2048]
+    Bs = {}
+    for N in set(shapes):
+        Bq, s = rmm.rmm_quantize_q8(up_bf16(weight_bits(K, N, seed=N)))
+        Bs[N] = (Bq, s, rmm.rmm_rownorms_q8(Bq, s))
+    r = 0.5
+    kk = rmm.rmm_kk(r, K)
+    need = max(rmm.rmm_gemm_q8_workspace_bytes(M, N, kk, gr) for N in shapes)
+    assert need > 0 and len({rmm.rmm_gemm_q8_workspace_bytes(M, N, kk, gr) for N in shapes}) > 1
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for N in shapes:
+        Bq, s, bn = Bs[N]
+        idx = rmm.rmm_select(A, r, gr, bnorm=bn)
+        Ap = rmm.rmm_gather(A, idx, kk, gr)[0]
+        Yw = rmm.rmm_gemm_q8(Ap, Bq, s, idx, kk, gr, ws=ws)
+        Yf = rmm.rmm_gemm_q8(Ap, Bq, s, idx, kk, gr)   # fresh zero-filled workspace
+        torch.cuda.synchronize()
+        assert np.array_equal(down(Yw), down(Yf)), f"reused workspace differs at N={N}"
