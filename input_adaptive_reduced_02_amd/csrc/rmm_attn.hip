@@ -69,28 +69,31 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 // ------------------------------------------------------------------ feature scores
 // scores[h][g][j] = binary32(sqrt(qsum) * sqrt(ksum)), qsum the sum of squares
 // of query column j over block g, ksum that of key column j over the block's
-// keys (the causal prefix, or every key; 1 without key norms).  The sums must
-// run in ascending row order in binary64 (each fma of an exact square rounds
-// once, like acc + x*x), so each is one dependent chain, and two kernels
-// split them:
-//   k_qk_ksum: one workgroup per head; waves 0-1 carry the 128 key chains
-//     through all L rows without a break, waves 2-3 DMA 128-row tiles into a
-//     4-slot LDS ring, three tiles ahead.  The running sums at the end of
-//     every block (causal) or at the end (every key) go to ksum.
-//   k_qk_qscore: one workgroup per (head, block); the block's query rows are
-//     staged in LDS, lane j sums its column and forms the score.
-// The key chains, L dependent fmas per lane, are the critical path.  (One
-// kernel with the key and query chains side by side, each fed through a
-// two-slot ring, measured slower: 57.9 us against 41.8 + 11.6 us at L = 4096.)
-constexpr int kKsumThreads = 256;
+// keys (the causal prefix, or every key; 1 without key norms).  The sums are
+// binary64 in a fixed order chosen for parallelism: within a 128-row tile,
+// four partial sums of the rows r = 0, 1, 2, 3 (mod 4) in ascending r, added
+// as (p0 + p1) + (p2 + p3); over the tiles of a prefix, the tile sums in
+// ascending tile order.  Every square of a bf16 value is exact in binary64,
+// so a sum of n of them differs from any other order's by at most about
+// n 2^-53 relative -- far inside the binary32 spacing of the score (2^-24),
+// so the binary32 scores agree with a plain ascending sum's to within one
+// unit in the last place, and only when the sum lies that close to a rounding
+// boundary.  Two kernels:
+//   k_qk_ktile: one workgroup per (head, key tile): the tile's column sums.
+//   k_qk_qscore: one workgroup per (head, query block): the block's query
+//     column sums, the prefix of the key tile sums, the product.
+// (One workgroup per head carrying the 128 key columns as L-step binary64
+// chains through the whole sequence took 41.9 us at L = 4096.)
 constexpr int kTileChunks = kQB * kHD / 8;   // 16-byte chunks of a 128 x 128 bf16 tile
 
-// acc += x*x for rows 0 .. rows-1 of column j of an LDS tile (row stride kHD), in order
-__device__ __forceinline__ void chain_tile(const uint16_t *t, int j, int rows, double &acc)
+// Sum of x*x over rows 0 .. rows-1 of column j of an LDS tile (row stride
+// kHD): four partial sums (row mod 4), each in ascending row order, then
+// (p0 + p1) + (p2 + p3).  The LDS reads of the next 16 rows are issued before
+// the fmas of the current 16.
+__device__ __forceinline__ double sumsq_tile(const uint16_t *t, int j, int rows)
 {
+    double p[4] = {0.0, 0.0, 0.0, 0.0};
     if (rows == kQB) {
-        // a whole tile: the LDS reads of the next 16 rows are issued before
-        // the fmas of the current 16, so only the fma chain is exposed
         uint16_t x[2][16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) x[0][u] = t[u * kHD + j];
@@ -104,23 +107,16 @@ __device__ __forceinline__ void chain_tile(const uint16_t *t, int j, int rows, d
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const double v = (double)bf16_to_f32(x[b & 1][u]);
-                acc = __builtin_fma(v, v, acc);
+                p[u & 3] = __builtin_fma(v, v, p[u & 3]);
             }
         }
-        return;
+    } else {
+        for (int r = 0; r < rows; ++r) {
+            const double v = (double)bf16_to_f32(t[r * kHD + j]);
+            p[r & 3] = __builtin_fma(v, v, p[r & 3]);
+        }
     }
-    int r = 0;
-    for (; r + 16 <= rows; r += 16) {
-        double x[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) x[u] = (double)bf16_to_f32(t[(r + u) * kHD + j]);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) acc = __builtin_fma(x[u], x[u], acc);
-    }
-    for (; r < rows; ++r) {
-        const double x = (double)bf16_to_f32(t[r * kHD + j]);
-        acc = __builtin_fma(x, x, acc);
-    }
+    return (p[0] + p[1]) + (p[2] + p[3]);
 }
 
 // 16-byte chunks lt + n*i (i < kTileChunks / n) of tile t of a [L][128] bf16
@@ -146,75 +142,25 @@ __device__ __forceinline__ void tile_store(uint16_t *buf, int lt, const u32x4 (&
     }
 }
 
-// DMA: every lane copies 16 bytes from its global address to LDS[lds + 16*lane]
-// (global_load_lds_dwordx4; no register result, waited for by an explicit
-// s_waitcnt).
-__device__ __forceinline__ void qk_dma16(const void *g, uint32_t lds)
+// tsum[h][t][j]: the sum of squares of key column j over key tile t of head h
+__global__ void __launch_bounds__(128)
+k_qk_ktile(const uint16_t *__restrict__ K, int64_t L, double *__restrict__ tsum)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void qk_vmwait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-
-template <int CAUSAL>
-__global__ void __launch_bounds__(kKsumThreads)
-k_qk_ksum(const uint16_t *__restrict__ K, int64_t L, double *__restrict__ ksum)
-{
-    constexpr int NB = 4;                         // LDS ring of key tiles
-    constexpr int BLK = kQB * kHD * 2 / 1024 / 2; // 1 KiB DMA blocks per loader wave per tile: 16
-    __shared__ __attribute__((aligned(1024))) uint16_t kt[NB][kQB * kHD];
-    const int64_t h = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const bool chain = tid < 128;                 // waves 0, 1: the chains; waves 2, 3: the loads
-    const int lw = __builtin_amdgcn_readfirstlane((tid >> 6) - 2);
+    constexpr int NCH = kTileChunks / 128;
+    __shared__ __attribute__((aligned(16))) uint16_t kt[kQB * kHD];
     const int64_t G = (L + kQB - 1) / kQB;
-    const uint16_t *Kh = K + h * L * kHD;
-    double *out = ksum + h * (CAUSAL ? G : 1) * kHD;
-    auto rows_of = [&](int64_t t) { return (int)((L - t * kQB < kQB) ? (L - t * kQB) : kQB); };
-    // this loader wave's half of tile t into ring slot t % NB: block b holds
-    // rows 4b .. 4b+3 (lane l: row 4b + l/16, bytes 16(l%16) ..); rows past L
-    // re-read row L-1, never summed
-    auto issue = [&](int64_t t) {
-        const uint32_t dst = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)kt[t % NB];
-#pragma unroll
-        for (int i = 0; i < BLK; ++i) {
-            const int b = lw * BLK + i;
-            int64_t row = t * kQB + 4 * b + (lane >> 4);
-            if (row > L - 1) row = L - 1;
-            qk_dma16(Kh + row * kHD + 8 * (lane & 15), dst + b * 1024);
-        }
-    };
-    // wait until tile t has landed, tiles t+1 and t+2 (if issued) in flight
-    auto wait_for = [&](int64_t t) {
-        if (t + 2 < G) qk_vmwait<2 * BLK>();
-        else if (t + 1 < G) qk_vmwait<BLK>();
-        else qk_vmwait<0>();
-    };
-
-    if (!chain) {
-        for (int64_t t = 0; t < 3 && t < G; ++t) issue(t);
-        wait_for(0);
-    }
+    const int64_t h = blockIdx.x / G, t = blockIdx.x % G;
+    const int j = threadIdx.x;
+    u32x4 v[NCH];
+    tile_load<NCH>(K + h * L * kHD, L, t, j, v);
+    tile_store<NCH>(kt, j, v);
     __syncthreads();
-    double acc = 0.0;
-    for (int64_t t = 0; t < G; ++t) {
-        // the chains sum tile t while the loaders fill slot (t+3) % NB, which
-        // held tile t-1 (summed before the last barrier), and wait for t+1
-        if (chain) {
-            chain_tile(kt[t % NB], tid, rows_of(t), acc);
-            if (CAUSAL) out[t * kHD + tid] = acc;   // the prefix of block t
-        } else if (t + 1 < G) {
-            if (t + 3 < G) issue(t + 3);
-            wait_for(t + 1);
-        }
-        __syncthreads();
-    }
-    if (!CAUSAL && chain) out[tid] = acc;
+    tsum[(h * G + t) * kHD + j] = sumsq_tile(kt, j, (int)((L - t * kQB < kQB) ? (L - t * kQB) : kQB));
 }
 
 template <int USE_K, int CAUSAL>
 __global__ void __launch_bounds__(128)
-k_qk_qscore(const uint16_t *__restrict__ Q, int64_t L, const double *__restrict__ ksum,
+k_qk_qscore(const uint16_t *__restrict__ Q, int64_t L, const double *__restrict__ tsum,
             float *__restrict__ scores)
 {
     constexpr int NCH = kTileChunks / 128;
@@ -225,26 +171,31 @@ k_qk_qscore(const uint16_t *__restrict__ Q, int64_t L, const double *__restrict_
     u32x4 v[NCH];
     tile_load<NCH>(Q + h * L * kHD, L, g, j, v);
     tile_store<NCH>(qt, j, v);
+    double ks = 0.0;
+    if (USE_K) {
+        // the key tiles the block is multiplied with, in ascending order
+        const double *ts = tsum + h * G * kHD + j;
+        const int64_t tend = CAUSAL ? g + 1 : G;
+        for (int64_t t = 0; t < tend; ++t) ks += ts[t * kHD];
+    }
     __syncthreads();
-    double qa = 0.0;
-    chain_tile(qt, j, (int)((L - g * kQB < kQB) ? (L - g * kQB) : kQB), qa);
-    const double kn = USE_K ? __builtin_sqrt(ksum[(h * (CAUSAL ? G : 1) + (CAUSAL ? g : 0)) * kHD + j]) : 1.0;
+    const double qa = sumsq_tile(qt, j, (int)((L - g * kQB < kQB) ? (L - g * kQB) : kQB));
+    const double kn = USE_K ? __builtin_sqrt(ks) : 1.0;
     scores[(h * G + g) * kHD + j] = (float)(__builtin_sqrt(qa) * kn);
 }
 
 hipError_t launch_qk_score(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int causal, int use_k,
-                           double *ksum, float *scores, hipStream_t s)
+                           double *tsum, float *scores, hipStream_t s)
 {
     const int64_t G = (L + kQB - 1) / kQB;
+    const dim3 grid((unsigned)(H * G)), block(128);
     if (use_k) {
-        if (causal) hipLaunchKernelGGL((k_qk_ksum<1>), dim3((unsigned)H), dim3(kKsumThreads), 0, s, K, L, ksum);
-        else hipLaunchKernelGGL((k_qk_ksum<0>), dim3((unsigned)H), dim3(kKsumThreads), 0, s, K, L, ksum);
+        hipLaunchKernelGGL(k_qk_ktile, grid, block, 0, s, K, L, tsum);
         if (hipError_t e = hipGetLastError()) return e;
     }
-    const dim3 grid((unsigned)(H * G)), block(128);
-    if (causal && use_k) hipLaunchKernelGGL((k_qk_qscore<1, 1>), grid, block, 0, s, Q, L, ksum, scores);
-    else if (use_k) hipLaunchKernelGGL((k_qk_qscore<1, 0>), grid, block, 0, s, Q, L, ksum, scores);
-    else hipLaunchKernelGGL((k_qk_qscore<0, 0>), grid, block, 0, s, Q, L, ksum, scores);
+    if (causal && use_k) hipLaunchKernelGGL((k_qk_qscore<1, 1>), grid, block, 0, s, Q, L, tsum, scores);
+    else if (use_k) hipLaunchKernelGGL((k_qk_qscore<1, 0>), grid, block, 0, s, Q, L, tsum, scores);
+    else hipLaunchKernelGGL((k_qk_qscore<0, 0>), grid, block, 0, s, Q, L, tsum, scores);
     return hipGetLastError();
 }
 
@@ -511,15 +462,18 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                 } else if (ht < 128) {
                     const int64_t k = kp0 + ht;
                     if (k < Kvalid) {
-                        double mass = 0.0;
+                        // eight partial sums (query mod 8), each in ascending q,
+                        // added pairwise: the chain is nq/8 adds long, not nq
+                        double m[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
                         for (int c = 0; c < nq / 8; ++c) {
                             const u32x4 v = *(const u32x4 *)&pb[ht * kPitch + 8 * c];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                mass += (double)bf16_lo(v[e]);
-                                mass += (double)bf16_hi(v[e]);
+                                m[2 * e] += (double)bf16_lo(v[e]);
+                                m[2 * e + 1] += (double)bf16_hi(v[e]);
                             }
                         }
+                        const double mass = ((m[0] + m[1]) + (m[2] + m[3])) + ((m[4] + m[5]) + (m[6] + m[7]));
                         pvs[(h * G + g) * L + k] = (float)(mass * vnorm[h * L + k]);
                     }
                 } else {

@@ -200,8 +200,9 @@ k_pv_vnorm(const uint16_t *__restrict__ V, int64_t HL, double *__restrict__ vnor
 // the wave reads the 64 key-major segments Pt[h][k][q0 .. q0+128) (256 B
 // each) with 16-byte loads that cover four whole segments per instruction;
 // the segments then pass through a small LDS slice half by half (queries
-// 0..63, then 64..127) so that lane l can sum segment l in ascending q in
-// binary64 -- the order a sequential sum takes -- and write
+// 0..63, then 64..127) so that lane l can sum segment l in binary64 -- eight
+// partial sums (query mod 8), each in ascending q, added pairwise, the order
+// the attention producer uses for the same scores -- and write
 // (float)(mass * ||V_k||).  The loads of the next item are issued before the
 // current item is summed.  Items that are not full (a short last query block
 // or a prefix ending inside the 64 keys) take a plain per-lane path.
@@ -277,7 +278,7 @@ k_pv_mass(const uint16_t *__restrict__ Pt, int64_t H, int64_t L, int64_t qblock,
         PvItem nxt{};
         if (nx < total) nxt = pv_item(nx * perm % total, L, qblock, causal, G, per_head);
         const int64_t k = cur.k0 + lane;
-        double mass = 0.0;
+        double m8[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};   // partial sums, query mod 8
         if (cur.full) {
             u32x4 hi[16];
 #pragma unroll
@@ -305,8 +306,8 @@ k_pv_mass(const uint16_t *__restrict__ Pt, int64_t H, int64_t L, int64_t qblock,
                     const u32x4 x = *(const u32x4 *)(row + 16 * j);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        mass += (double)bf16_lo(x[e]);
-                        mass += (double)bf16_hi(x[e]);
+                        m8[2 * e] += (double)bf16_lo(x[e]);
+                        m8[2 * e + 1] += (double)bf16_hi(x[e]);
                     }
                 }
             }
@@ -314,7 +315,7 @@ k_pv_mass(const uint16_t *__restrict__ Pt, int64_t H, int64_t L, int64_t qblock,
         } else {
             if (k < cur.Kg) {
                 const uint16_t *src = Pt + (cur.h * L + k) * L + cur.q0;
-                for (int64_t i = 0; i < cur.nq; ++i) mass += (double)bf16_to_f32(src[i]);
+                for (int64_t i = 0; i < cur.nq; ++i) m8[i & 7] += (double)bf16_to_f32(src[i]);
             }
             if (nx < total && nxt.full) {
 #pragma unroll
@@ -322,6 +323,7 @@ k_pv_mass(const uint16_t *__restrict__ Pt, int64_t H, int64_t L, int64_t qblock,
                     v[i] = *(const u32x4 *)(Pt + (nxt.h * L + nxt.k0 + 4 * i + (lane >> 4)) * L + nxt.q0 + 8 * c);
             }
         }
+        const double mass = ((m8[0] + m8[1]) + (m8[2] + m8[3])) + ((m8[4] + m8[5]) + (m8[6] + m8[7]));
         if (k < cur.Kg) scores[(cur.h * G + cur.g) * L + k] = (float)(mass * vnorm[cur.h * L + k]);
         cur = nxt;
         it = nx;

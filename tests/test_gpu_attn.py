@@ -6,9 +6,14 @@ and the P.V key scores the producer forms from its own stored probabilities.
 Inputs: Q, K, V bf16 N(0,1) [H, L, D = 128] (synth.pv_qkv).
 
 Bars:
-  - feature scores and P.V key scores bit-exact (the P.V scores against the
-    oracle evaluated on the probabilities the GPU stored);
-  - kept feature and key sets exact outside the near-tie band;
+  - feature scores and P.V key scores within one binary32 ulp of the
+    oracle's (the P.V scores against the oracle evaluated on the
+    probabilities the GPU stored): the GPU sums in binary64 in a fixed order
+    of its own (partial sums added pairwise), the oracle in ascending order,
+    and the two binary64 sums differ by about n 2^-53 relative;
+  - kept feature and key sets identical where the two sides' keys are
+    bit-identical; elsewhere the GPU's set is the kk best of its own keys and
+    differs from the oracle's only inside the near-tie band;
   - probabilities within the bound derived from the arithmetic, per element:
       |P_gpu - P_ref| <= 1.01 [ (2^-8 + e) P_ref ] + 2^-126
     2^-8: rounding to bf16; e: relative error of the binary32 value before
@@ -26,7 +31,7 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import DEV, check_output, compare_sets, down, log, up_bf16
+from gpu_util import DEV, check_output, compare_scores_ulp, compare_sets_keys, down, log, up_bf16
 from input_adaptive_reduced_02_amd import rmm, synth
 
 pytestmark = pytest.mark.gpu
@@ -76,10 +81,10 @@ def check_block(q, k, v, idx_np, qs_np, Pt_np, pvs_np, h, g, L, r_qk, causal, us
     kept = None
     if r_qk < 1.0:
         sel = O.qk_select_block(Qh, Kh, QB, g, r_qk, causal, use_k)
-        assert np.array_equal(qs_np[h, g], sel["s32"]), f"{tag} h={h} g={g}: feature scores differ"
+        compare_scores_ulp(qs_np[h, g], sel["s32"], f"{tag} h={h} g={g} feature scores")
         kk = sel["kk"]
-        compare_sets(idx_np[h * (-(-L // QB)) + g, :kk], dict(idx={g: sel["idx"]}, near={g: sel["near"]}), g, kk,
-                     f"{tag} h={h}")
+        compare_sets_keys(idx_np[h * (-(-L // QB)) + g, :kk], qs_np[h, g], sel["idx"], sel["s32"], sel["near"], kk,
+                          f"{tag} h={h} g={g} features")
         kept = idx_np[h * (-(-L // QB)) + g, :kk].astype(np.int32)
     feats = np.arange(D, dtype=np.int32) if kept is None else kept
     out = {}
@@ -101,7 +106,7 @@ def check_block(q, k, v, idx_np, qs_np, Pt_np, pvs_np, h, g, L, r_qk, causal, us
     if pvs_np is not None:
         Ptb = O.widen_bf16(Pt_np[h, :Kg, q0:q0 + nq])
         _, s32 = O.pv_scores(Ptb, O.widen_bf16(v[h])[:Kg])
-        assert np.array_equal(pvs_np[h, g, :Kg], s32), f"{tag} h={h} g={g}: P.V scores differ"
+        compare_scores_ulp(pvs_np[h, g, :Kg], s32, f"{tag} h={h} g={g} P.V scores")
     return out
 
 
@@ -173,6 +178,15 @@ def test_chain_small():
     q, k, v, Qd, Kd, Vd = make_qkv(H, L, seed=7)
     idx, qs, Pt, pvs = run_producer(Qd, Kd, Vd, 0.5, True)
     G = -(-L // QB)
+    # the producer's key scores and the P.V path's block scores over the same
+    # stored P sum in the same order: equal bit for bit on every candidate key
+    sc2 = torch.zeros((H, G, L), dtype=torch.float32, device=DEV)
+    rmm.rmm_pv_select(Pt, Vd, 0.5, QB, True, scores_out=sc2)
+    torch.cuda.synchronize()
+    a, b = down(pvs), down(sc2)
+    for g in range(G):
+        Kg = O.pv_prefix(L, QB, g, True)
+        assert np.array_equal(a[:, g, :Kg].view(np.uint32), b[:, g, :Kg].view(np.uint32)), f"block {g}"
     for r in (0.3, 0.5):
         kidx = rmm.rmm_pv_select_scores(pvs, r, QB, True)
         O_ = rmm.rmm_pv_gemm(Pt, Vd, r, kidx, QB, True)
@@ -186,11 +200,11 @@ def test_chain_small():
                 Kg = O.pv_prefix(L, QB, g, True)
                 Ptb = O.widen_bf16(Pt_np[h, :Kg, q0:q0 + nq])
                 s64, s32 = O.pv_scores(Ptb, Vh[:Kg])
-                assert np.array_equal(pvs_np[h, g, :Kg], s32)
+                compare_scores_ulp(pvs_np[h, g, :Kg], s32, f"chain r={r} h={h} g={g} P.V scores")
                 kk = O.kk(r, Kg)
                 ref = O.topk(s32, kk)
-                compare_sets(kidx_np[h * G + g, :kk], dict(idx={g: ref}, near={g: O.near_ties(s64, s32, ref)}), g, kk,
-                             f"chain r={r} h={h}")
+                compare_sets_keys(kidx_np[h * G + g, :kk], pvs_np[h, g, :Kg], ref, s32, O.near_ties(s64, s32, ref),
+                                  kk, f"chain r={r} h={h} g={g} keys")
                 kept = kidx_np[h * G + g, :kk].astype(np.int32)
                 Ob = O.pv_block(Ptb, Vh[:Kg], kept)
                 Sb = O.pv_block(np.abs(Ptb), np.abs(Vh[:Kg]), kept)
@@ -210,8 +224,9 @@ def test_full_size_sampled():
         Qh, Kh = O.widen_bf16(q[h]), O.widen_bf16(k[h])
         for g in range(G):
             sel = O.qk_select_block(Qh, Kh, QB, g, 0.5, True, True)
-            assert np.array_equal(qs_np[h, g], sel["s32"]), f"h={h} g={g}: feature scores differ"
-            compare_sets(idx_np[h * G + g, :64], dict(idx={g: sel["idx"]}, near={g: sel["near"]}), g, 64, f"full h={h}")
+            compare_scores_ulp(qs_np[h, g], sel["s32"], f"full h={h} g={g} feature scores")
+            compare_sets_keys(idx_np[h * G + g, :64], qs_np[h, g], sel["idx"], sel["s32"], sel["near"], 64,
+                              f"full h={h} g={g} features")
     for h in (0, 31):
         Pt_h = down(Pt[h])
         Pt_np = Pt_h[None]
@@ -264,13 +279,12 @@ def test_long_sequence_sampled():
             check_block(q[h:h + 1], k[h:h + 1], v[h:h + 1], idx_np[h * G:(h + 1) * G], qs_np[h:h + 1], Pt_np,
                         pvs_np[h:h + 1], 0, g, L, 0.5, True, True, f"long h={h}")
             Kg = O.pv_prefix(L, QB, g, True)
-            s32 = pvs_np[h, g, :Kg]
             kk = O.kk(0.5, Kg)
-            ref = O.topk(s32, kk)
             Ptb = O.widen_bf16(Pt_np[0, :Kg, g * QB:(g + 1) * QB])
-            s64, _ = O.pv_scores(Ptb, O.widen_bf16(v[h])[:Kg])
-            compare_sets(kidx_np[h * G + g, :kk], dict(idx={g: ref}, near={g: O.near_ties(s64, s32, ref)}), g, kk,
-                         f"long keys h={h}")
+            s64, s32 = O.pv_scores(Ptb, O.widen_bf16(v[h])[:Kg])
+            ref = O.topk(s32, kk)
+            compare_sets_keys(kidx_np[h * G + g, :kk], pvs_np[h, g, :Kg], ref, s32, O.near_ties(s64, s32, ref), kk,
+                              f"long keys h={h} g={g}")
         del Pt_np
 
 

@@ -3,15 +3,19 @@ against the oracle, through the C ABI.
 
 P is the causal row-softmax of Q K^T / sqrt(128) made by synth.pv_probs_t on
 the device, stored key-major; its bits are the input of both sides (the oracle
-reads them back, it does not recompute the softmax).  Block scores and kept
-sets must be bit-exact; outputs within the bound of tests/gpu_util.py.
+reads them back, it does not recompute the softmax).  Block scores within one
+binary32 ulp of the oracle's (the GPU sums each key's probabilities in
+binary64 as eight partial sums added pairwise, the oracle in ascending
+order); kept sets identical where the keys are, otherwise the kk best of the
+GPU's own keys and different only inside the near-tie band; outputs within
+the bound of tests/gpu_util.py.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from gpu_util import DEV, check_output, compare_sets, down, log, up_bf16, widen
+from gpu_util import DEV, check_output, compare_scores_ulp, compare_sets_keys, down, log, up_bf16, widen
 from input_adaptive_reduced_02_amd import rmm, synth
 
 pytestmark = pytest.mark.gpu
@@ -50,11 +54,11 @@ def check_block(Pt_h, V_h, O_h, idx_h, scores_h, L, g, r, causal, tag, q_sample=
     Ptb = O.widen_bf16(Pt_h[:Kg, q0:q0 + nq])
     if r < 1:
         s64, s32 = O.pv_scores(Ptb, Vh64[:Kg])
-        assert np.array_equal(scores_h[g, :Kg], s32), f"{tag} block {g}: scores differ"
+        compare_scores_ulp(scores_h[g, :Kg], s32, f"{tag} block {g} scores")
         kk = O.kk(r, Kg)
         ref_idx = O.topk(s32, kk)
-        sel = dict(idx={g: ref_idx}, near={g: O.near_ties(s64, s32, ref_idx)})
-        compare_sets(idx_h[g, :kk], sel, g, kk, f"{tag} block {g}")
+        compare_sets_keys(idx_h[g, :kk], scores_h[g, :Kg], ref_idx, s32, O.near_ties(s64, s32, ref_idx), kk,
+                          f"{tag} block {g}")
         kpad = -(-kk // 64) * 64
         assert np.all(idx_h[g, kk:kpad] == idx_h[g, kk - 1]), f"{tag} block {g}: padding"
 
