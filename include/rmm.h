@@ -19,8 +19,11 @@
  *     may be short); a whole matrix is one group when group_rows >= M;
  *   - kk = rmm_kk(r, K) (ceil(r*K) for decimal r, see below);
  *   - equal scores go to the lower index;
- *   - scores are accumulated in binary64 in ascending row order and rounded
- *     once to binary32, which is the precision of the keep/drop decision;
+ *   - scores are accumulated in binary64 and rounded once to binary32, which
+ *     is the precision of the keep/drop decision: the linear path's column
+ *     norms in ascending row order, the attention-side sums (QK^T feature
+ *     norms, P.V key masses) in a fixed order of partial sums added pairwise
+ *     (within one binary32 ulp of an ascending sum);
  *   - P.V: per query block g the candidate keys are the causal prefix
  *     k < min(L, qblock*(g+1)); score = block column mass of P * ||V[k, :]||_2.
  *
@@ -238,6 +241,7 @@ size_t rmm_attn_pv_workspace_bytes(int64_t H, int64_t L, int64_t D, double r, in
  * q0 = g*qblock .. min(L, q0+qblock)-1), with candidate keys k < K_g
  * (K_g = min(L, qblock*(g+1)) if causal, else L):
  *   score[h][g][k] = binary32( (sum_{q in block} P[h][q][k]) * ||V[h][k][:]||_2 )
+ * (the sum in binary64 as eight partial sums, query mod 8, added pairwise)
  *   I = the kk_g = rmm_kk(r, K_g) best keys (ties to the lower index)
  *   O[h][q][:] = sum_{k in I} P[h][q][k] * V[h][k][:]
  * r == 1 skips scoring and selection: the dense causal product, same kernel.
@@ -332,14 +336,16 @@ int rmm_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int64_t ldq, c
  * rmm_qk_select: per (head h, block g), feature j scores
  *   s[h][g][j] = binary32( ||Q[h][block, j]||_2 * ||K[h][0 .. K_g-1, j]||_2 )
  * (use_k == 0: the first factor alone, the pages' activation-only rule), each
- * norm summed in ascending order in binary64; the kk = rmm_kk(r, D) best
+ * sum of squares in binary64 -- per 128-row tile four partial sums (row mod
+ * 4, ascending) added as (p0 + p1) + (p2 + p3), a causal prefix as the
+ * ascending sum of its tiles' sums; the kk = rmm_kk(r, D) best
  * features are kept (ties to the lower index) and written ascending to
  * idx_out[h*G + g][0 .. kk-1], padded by repeating the last one up to
  * rmm_kk_pad(kk).  0 < r <= 1; ldidx_out % 4 == 0, >= rmm_kk_pad(D).
  * scores_out [H][G][D] binary32 or NULL (then the workspace holds them).
  * The workspace (rmm_qk_select_workspace_bytes, 16-byte aligned, device)
- * always holds the binary64 key sums of squares, H*G*D*8 bytes rounded up to
- * 256, followed by the scores when scores_out is NULL. */
+ * always holds the binary64 key sums of squares per 128-key tile, H*G*D*8
+ * bytes rounded up to 256, followed by the scores when scores_out is NULL. */
 size_t rmm_qk_select_workspace_bytes(int64_t H, int64_t L, int64_t D, int64_t qblock, int have_scores_out);
 int rmm_qk_select(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, int64_t D, double r,
                   int64_t qblock, int causal, int use_k, int32_t *idx_out, int64_t ldidx_out,
@@ -355,9 +361,10 @@ int rmm_qk_select(const uint16_t *Q, const uint16_t *K, int64_t H, int64_t L, in
  * every block's candidate keys (0 where k > q); entries past a block's
  * candidates are not written.  Pt is [H][L][L].
  * pv_scores [H][G][L] binary32 or NULL: for k < K_g,
- *   pv_scores[h][g][k] = binary32( (sum over the block's queries, ascending,
- *                                   of the stored P[q][k]) * ||V[h][k][:]||_2 )
- * in binary64 -- the scores rmm_attn_pv forms from Pt, here without reading
+ *   pv_scores[h][g][k] = binary32( (sum over the block's queries of the
+ *                                   stored P[q][k]) * ||V[h][k][:]||_2 )
+ * in binary64, the sum as eight partial sums (query mod 8, ascending) added
+ * pairwise -- the scores rmm_attn_pv forms from Pt, bit for bit, here without reading
  * Pt again; V is then required.  Workspace:
  * rmm_attn_probs_workspace_bytes(H, L, D, pv_scores != NULL) bytes. */
 size_t rmm_attn_probs_workspace_bytes(int64_t H, int64_t L, int64_t D, int have_pv_scores);
