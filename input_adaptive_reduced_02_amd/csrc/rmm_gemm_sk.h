@@ -213,6 +213,31 @@ k_gemm_sk(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
     }
     vmwait<0>();   // the trailing reloads: no DMA may land after the workgroup ends
 
+    if (ydt == 1) {
+        // bf16 output: the 64 x 128 tile staged in LDS (the ring is free once
+        // every wave has passed the barrier below), written as whole 16-byte
+        // row chunks with streaming stores (N % 8 == 0: a chunk never crosses N)
+        constexpr int PITCH = TN * 2 + 16;   // bytes per staged row; +16 spreads rows over the banks
+        static_assert(TM * PITCH <= S::NSTAGE * S::STAGE_ELEMS * 2, "staged tile fits the ring");
+        char *st = (char *)smem;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = fm * 32 + acc_row(lane, v), c = wave * WN + acc_col(lane);
+                *(uint16_t *)(st + r * PITCH + 2 * c) = (uint16_t)f32_to_bf16(acc[fm][v]);
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int e = threadIdx.x; e < TM * (TN / 8); e += 64 * S::NW) {
+            const int r = e / (TN / 8), ch = e % (TN / 8);
+            const int64_t row = row0 + r, cl = col0 + 8 * ch;
+            if (row < row_end && cl < N)
+                __builtin_nontemporal_store(*(const u32x4 *)(st + r * PITCH + 16 * ch),
+                                            (u32x4 *)((uint16_t *)Y + row * ldy + cl));
+        }
+        return;
+    }
     const int64_t col = col0 + wave * WN + acc_col(lane);
     if (col < N) {
 #pragma unroll
@@ -221,10 +246,7 @@ k_gemm_sk(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
             for (int v = 0; v < 16; ++v) {
                 const int64_t row = row0 + fm * 32 + acc_row(lane, v);
                 if (row >= row_end) continue;
-                if (ydt == 1)
-                    ((uint16_t *)Y)[row * ldy + col] = (uint16_t)f32_to_bf16(acc[fm][v]);
-                else
-                    ((float *)Y)[row * ldy + col] = acc[fm][v];
+                ((float *)Y)[row * ldy + col] = acc[fm][v];
             }
         }
     }

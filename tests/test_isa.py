@@ -108,6 +108,7 @@ NT_STREAMS = [
     ("rmm_attn.hip", "k_attn_probs", "global_store_dwordx4", True),
     ("rmm_pv.hip", "k_pv_gemm", "global_load_lds_dwordx4", True),
     ("rmm_gemm.hip", "k_gemm_sk", "global_load_lds_dwordx4", True),
+    ("rmm_gemm.hip", "k_gemm_sk", "global_store_dwordx4", True),
     ("rmm_q8.hip", "k_gemm_q8", "global_load_lds_dwordx4", True),
     ("rmm_gemm.hip", "k_gemm_dl", "global_store_dwordx4", False),
     ("rmm_gemm.hip", "k_gemm_wt", "global_store_dwordx4", True),
