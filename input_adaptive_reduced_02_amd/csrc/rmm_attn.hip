@@ -6,7 +6,7 @@
 // of QK^T and, optionally, the token dimension of PV.  For head h and query
 // block g (128 queries, candidate keys k < K_g: the causal prefix, or every
 // key without the mask):
-//   feature score  s_j = ||Q[block, j]||_2 * ||K[0 .. K_g-1, j]||_2   (k_qk_ksum, k_qk_qscore)
+//   feature score  s_j = ||Q[block, j]||_2 * ||K[0 .. K_g-1, j]||_2   (k_qk_ktile, k_qk_qscore)
 //   kept features  I   = the kk = ceil(r D) best (the shared select kernel)
 //   logits         S[q, k] = sum_{j in I} Q[q, j] K[k, j] / sqrt(D)
 //   probabilities  P[q, .] = softmax of row q over its keys (k <= q causal)
