@@ -50,11 +50,11 @@
 namespace rmm {
 
 constexpr int kBuckets = 2048;
-constexpr int kNW = kSelectThreads / 64;
 
-// Sum of a wave-uniform value over the workgroup's waves; every thread gets
+// Sum of a wave-uniform value over the workgroup's NW waves; every thread gets
 // the result.  `slot` is one of two alternating LDS rows, so consecutive calls
 // need a single barrier each.
+template <int NW>
 __device__ __forceinline__ uint64_t block_sum_uniform(uint64_t v, uint64_t *slot)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -62,14 +62,15 @@ __device__ __forceinline__ uint64_t block_sum_uniform(uint64_t v, uint64_t *slot
     __syncthreads();
     uint64_t s = 0;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) s += slot[w];
+    for (int w = 0; w < NW; ++w) s += slot[w];
     return s;
 }
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
 
-// Exclusive prefix sum of a per-thread value v < 2^16 over the workgroup
-// (thread order), plus the total.  Uses ballots on the bits of v.
+// Exclusive prefix sum of a per-thread value v < 2^16 over the workgroup of
+// NW waves (thread order), plus the total.  Uses ballots on the bits of v.
+template <int NW>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wtot, uint32_t &total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -86,7 +87,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wtot, 
     uint32_t before = 0;
     total = 0;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) {
+    for (int w = 0; w < NW; ++w) {
         const uint32_t x = wtot[w];
         before += (w < wave) ? x : 0;
         total += x;
@@ -121,22 +122,27 @@ __device__ __forceinline__ uint32_t sel_lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
-// NRB = 0: selection only, one workgroup per group.  NRB > 0: selection and
-// gather, `ga.slices` workgroups per group, each staging at most NRB 1 KiB
-// blocks of rows per wave (16 * NRB KiB per workgroup).
-template <int KPT, int NRB>
-__global__ void __launch_bounds__(kSelectThreads)
+// NRB = 0: selection only, one workgroup of NT threads per group (1024 for a
+// few long groups: latency; 256 for many groups: several workgroups per CU and
+// 4-wave barriers).  NRB > 0: selection and gather, `ga.slices` 1024-thread
+// workgroups per group, each staging at most NRB 1 KiB blocks of rows per
+// wave (16 * NRB KiB per workgroup).
+template <int KPT, int NRB, int NT>
+__global__ void __launch_bounds__(NT)
 k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__ idx, int64_t ldidx,
          float *__restrict__ thresh, double *__restrict__ bound, SelectGather ga)
 {
+    constexpr int NW = NT / 64, BPT = kBuckets / NT;   // waves; histogram buckets per thread
+    static_assert(NRB == 0 || NT == kSelectThreads, "the fused gather runs 1024-thread workgroups");
+    static_assert(BPT >= 2 && kBuckets % NT == 0, "a thread scans whole buckets");
     __shared__ uint32_t hist[kBuckets];
-    __shared__ __attribute__((aligned(16))) int32_t cand[KPT * kSelectThreads];   // later the kept list
+    __shared__ __attribute__((aligned(16))) int32_t cand[KPT * NT];   // later the kept list
     __shared__ __attribute__((aligned(1024))) unsigned char stage[NRB > 0 ? NRB * 16 * 1024 : 16];
-    __shared__ uint64_t red[2][kNW];
-    __shared__ uint64_t wsum64[kNW];
-    __shared__ uint32_t wtot[kNW];
-    __shared__ int32_t imin[kNW], imax[kNW];
-    __shared__ double fsum[kNW];
+    __shared__ uint64_t red[2][NW];
+    __shared__ uint64_t wsum64[NW];
+    __shared__ uint32_t wtot[NW];
+    __shared__ int32_t imin[NW], imax[NW];
+    __shared__ double fsum[NW];
     __shared__ int32_t s_last, s_bin;
     __shared__ uint32_t s_nc;
     __shared__ int64_t s_above;
@@ -155,10 +161,15 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     }
     const float *s = scores + grp * sh.lds;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int kpt = (int)((K + kSelectThreads - 1) / kSelectThreads);
+    // keys per thread, a multiple of 4 where KPT allows (KPT is a power of
+    // two >= the plain quotient), so full runs take 16-byte loads: K = 14336
+    // gives 896 threads of 16 keys rather than 1024 of 14 (4-byte loads at a
+    // 56-byte lane stride)
+    const int kpt0 = (int)((K + NT - 1) / NT);
+    const int kpt = KPT >= 4 ? (kpt0 + 3) & ~3 : kpt0;
     const int64_t base = (int64_t)tid * kpt;
 
-    for (int i = tid; i < kBuckets; i += kSelectThreads) hist[i] = 0;
+    for (int i = tid; i < kBuckets; i += NT) hist[i] = 0;
     if (tid == 0) {
         s_last = 0;   // written again (by the kk-th keeper) after several barriers
         s_nc = 0;     // candidate count, first added to after two barriers
@@ -199,7 +210,7 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     }
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) {
+    for (int w = 0; w < NW; ++w) {
         lo = min(lo, imin[w]);
         hi = max(hi, imax[w]);
     }
@@ -215,17 +226,24 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         if (key[i] >= 0) atomicAdd(&hist[bucket(key[i])], 1u);
     __syncthreads();
     {
-        // thread t owns buckets 2t, 2t+1
-        const uint32_t hlo = hist[2 * tid], hhi = hist[2 * tid + 1];
+        // thread t owns buckets BPT t .. BPT t + BPT - 1 and walks them from
+        // the top; exactly one bucket holds the kk-th largest key
+        uint32_t h[BPT], mine = 0;
+#pragma unroll
+        for (int b = 0; b < BPT; ++b) {
+            h[b] = hist[BPT * tid + b];
+            mine += h[b];
+        }
         uint32_t total;
-        const uint32_t incl = block_excl_scan(hlo + hhi, wtot, total) + hlo + hhi;
-        const int64_t above = (int64_t)total - incl;   // keys in buckets above 2t+1
-        if (above < kk && kk <= above + hhi) {
-            s_bin = 2 * tid + 1;
-            s_above = above;
-        } else if (above + hhi < kk && kk <= above + hhi + hlo) {
-            s_bin = 2 * tid;
-            s_above = above + hhi;
+        const uint32_t incl = block_excl_scan<NW>(mine, wtot, total) + mine;
+        int64_t above = (int64_t)total - incl;   // keys in buckets above this thread's
+#pragma unroll
+        for (int b = BPT - 1; b >= 0; --b) {
+            if (above < kk && kk <= above + h[b]) {
+                s_bin = BPT * tid + b;
+                s_above = above;
+            }
+            above += h[b];
         }
     }
     __syncthreads();
@@ -251,7 +269,7 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         const uint32_t st0 = sel_lds_addr(stage);
 #pragma unroll
         for (int i = 0; i < NRB; ++i) {
-            const int b = wv + kNW * i;
+            const int b = wv + NW * i;
             const int64_t o = (int64_t)b * 1024 + 16 * lane;
             if ((int64_t)b * 1024 < sbytes) sel_dma16(o < sbytes ? src + o : src, st0 + b * 1024);
         }
@@ -334,14 +352,12 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     } else {
         int round = 0;
         for (int sh2 = 29; sh2 >= 1; sh2 -= 2, ++round) {
-            const uint64_t c = block_sum_uniform(
-                count3(cand, tid, n1, kSelectThreads, T | (1 << sh2), T | (2 << sh2), T | (3 << sh2)),
-                red[round & 1]);
+            const uint64_t c = block_sum_uniform<NW>(
+                count3(cand, tid, n1, NT, T | (1 << sh2), T | (2 << sh2), T | (3 << sh2)), red[round & 1]);
             const int64_t t1 = c & 0x1fffff, t2 = (c >> 21) & 0x1fffff, t3 = c >> 42;
             T |= ((t3 >= need) ? 3 : (t2 >= need) ? 2 : (t1 >= need) ? 1 : 0) << sh2;
         }
-        const uint64_t c = block_sum_uniform(count3(cand, tid, n1, kSelectThreads, T | 1, T | 1, T | 1),
-                                             red[round & 1]);
+        const uint64_t c = block_sum_uniform<NW>(count3(cand, tid, n1, NT, T | 1, T | 1, T | 1), red[round & 1]);
         if ((int64_t)(c & 0x1fffff) >= need) T |= 1;
     }
 
@@ -359,7 +375,7 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     __syncthreads();
     uint64_t before = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) {
+    for (int w = 0; w < NW; ++w) {
         const uint64_t x = wsum64[w];
         before += (w < wave) ? x : 0;
         total += x;
@@ -381,10 +397,9 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
             ++eq_seen;
         }
         if (keep) {
-            if (pos < kk) {   // always true when T is the kk-th key
-                if constexpr (NRB > 0) cand[pos] = k;   // every reader of cand passed a barrier since
-                else out[pos] = k;
-            }
+            // the kept list goes to LDS (every reader of cand passed a barrier
+            // since) and leaves in one coalesced copy after the last barrier
+            if (pos < kk) cand[pos] = k;   // always true when T is the kk-th key
             if (pos == kk - 1) s_last = k;
             ++pos;
         } else {
@@ -398,15 +413,17 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         if (lane == 0) fsum[wave] = dropped;
     }
     if constexpr (NRB > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's row blocks
-    __syncthreads();
+    // LDS-only barrier: the kept list, fsum and s_last are in LDS; the one
+    // global store issued so far (thresh) is read by no one here, so there is
+    // no need to wait for it as __syncthreads would
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int64_t padded = pad_up(kk);
     if (lead) {
-        if constexpr (NRB > 0)
-            for (int64_t j = tid; j < kk; j += kSelectThreads) out[j] = cand[j];
-        for (int64_t j = kk + tid; j < padded; j += kSelectThreads) out[j] = s_last;
+        for (int64_t j = tid; j < kk; j += NT) out[j] = cand[j];
+        for (int64_t j = kk + tid; j < padded; j += NT) out[j] = s_last;
         if (bound && tid == 0) {
             double b = 0.0;
-            for (int w = 0; w < kNW; ++w) b += fsum[w];
+            for (int w = 0; w < NW; ++w) b += fsum[w];
             bound[grp] = b;
         }
     }
@@ -417,7 +434,7 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         // tid + 1024, ..., stepped without division
         const int cpr = (int)(padded / 8);
         const int kk32 = (int)kk;
-        const int di = kSelectThreads / cpr, dc = kSelectThreads % cpr;
+        const int di = NT / cpr, dc = NT % cpr;
         int i = tid / cpr, c = tid % cpr;
         for (; i < nrows; i += di, c += dc) {
             if (c >= cpr) {
@@ -652,28 +669,36 @@ k_select_wave(const float *__restrict__ scores, SelectShape sh, int32_t *__restr
 hipError_t launch_select(const float *scores, const SelectShape &sh, int32_t *idx, int64_t ldidx,
                          float *thresh, double *bound, hipStream_t s)
 {
-    dim3 grid((unsigned)sh.groups), block(kSelectThreads);
-    // Many groups (the P.V blocks): one wave per group, many groups per CU at
-    // once -- throughput.  Few groups: one 1024-thread workgroup each, whose
-    // 16 waves finish a group sooner than a single wave does -- latency.
-    if (sh.groups >= 512 && sh.K <= 64 * 128) {
-        const int64_t kw = (sh.K + 63) / 64;
-#define RMM_SELECT_WAVE(N) \
-    hipLaunchKernelGGL(k_select_wave<N>, grid, dim3(64), 0, s, scores, sh, idx, ldidx, thresh, bound)
-        if (kw <= 4) RMM_SELECT_WAVE(4);
-        else if (kw <= 8) RMM_SELECT_WAVE(8);
-        else if (kw <= 16) RMM_SELECT_WAVE(16);
-        else if (kw <= 32) RMM_SELECT_WAVE(32);
-        else if (kw <= 64) RMM_SELECT_WAVE(64);
-        else RMM_SELECT_WAVE(128);
-#undef RMM_SELECT_WAVE
+    const dim3 grid((unsigned)sh.groups);
+    // Many short groups (the QK feature lists: 128 candidates): one wave per
+    // group, many groups per CU at once.
+    if (sh.groups >= 512 && sh.K <= 256) {
+        hipLaunchKernelGGL(k_select_wave<4>, grid, dim3(64), 0, s, scores, sh, idx, ldidx, thresh, bound);
         return hipGetLastError();
     }
+    // Many longer groups (the P.V key lists, up to L keys): 256-thread
+    // workgroups, several per CU, 4-wave barriers; a long group no longer
+    // rests on one wave (L = 4096: 35 us with one wave per group).
+    if (sh.groups >= 512 && sh.K <= 64 * 256) {
+        const int64_t kpt = (sh.K + 255) / 256;
+#define RMM_SELECT_256(N) \
+    hipLaunchKernelGGL((k_select<N, 0, 256>), grid, dim3(256), 0, s, scores, sh, idx, ldidx, thresh, bound, SelectGather{})
+        if (kpt <= 2) RMM_SELECT_256(2);
+        else if (kpt <= 4) RMM_SELECT_256(4);
+        else if (kpt <= 8) RMM_SELECT_256(8);
+        else if (kpt <= 16) RMM_SELECT_256(16);
+        else if (kpt <= 32) RMM_SELECT_256(32);
+        else RMM_SELECT_256(64);
+#undef RMM_SELECT_256
+        return hipGetLastError();
+    }
+    // Few groups: one 1024-thread workgroup each, whose 16 waves finish a
+    // group soonest -- latency.
     const int64_t kpt = (sh.K + kSelectThreads - 1) / kSelectThreads;
-#define RMM_SELECT_LAUNCH(N) \
-    hipLaunchKernelGGL((k_select<N, 0>), grid, block, 0, s, scores, sh, idx, ldidx, thresh, bound, SelectGather{})
-    if (kpt <= 1) RMM_SELECT_LAUNCH(1);
-    else if (kpt <= 2) RMM_SELECT_LAUNCH(2);
+#define RMM_SELECT_LAUNCH(N)                                                                              \
+    hipLaunchKernelGGL((k_select<N, 0, kSelectThreads>), grid, dim3(kSelectThreads), 0, s, scores, sh, idx, ldidx, \
+                       thresh, bound, SelectGather{})
+    if (kpt <= 2) RMM_SELECT_LAUNCH(2);
     else if (kpt <= 4) RMM_SELECT_LAUNCH(4);
     else if (kpt <= 8) RMM_SELECT_LAUNCH(8);
     else if (kpt <= 16) RMM_SELECT_LAUNCH(16);
@@ -716,7 +741,7 @@ hipError_t launch_select_gather(const float *scores, const SelectShape &sh, int3
     dim3 grid((unsigned)(sh.groups * ga.slices)), block(kSelectThreads);
     const int64_t kpt = (sh.K + kSelectThreads - 1) / kSelectThreads;
 #define RMM_SG_LAUNCH(N, R) \
-    hipLaunchKernelGGL((k_select<N, R>), grid, block, 0, s, scores, sh, idx, ldidx, thresh, bound, ga)
+    hipLaunchKernelGGL((k_select<N, R, kSelectThreads>), grid, block, 0, s, scores, sh, idx, ldidx, thresh, bound, ga)
 #define RMM_SG_NRB(N)                        \
     do {                                     \
         if (nrb == 1) RMM_SG_LAUNCH(N, 1);   \
