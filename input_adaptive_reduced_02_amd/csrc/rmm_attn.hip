@@ -170,14 +170,23 @@ k_qk_qscore(const uint16_t *__restrict__ Q, int64_t L, const double *__restrict_
     const int j = threadIdx.x;
     u32x4 v[NCH];
     tile_load<NCH>(Q + h * L * kHD, L, g, j, v);
-    tile_store<NCH>(qt, j, v);
     double ks = 0.0;
     if (USE_K) {
-        // the key tiles the block is multiplied with, in ascending order
+        // the key tiles the block is multiplied with, added in ascending
+        // order; the loads of 16 tiles are issued before their adds (and the
+        // first ones while the query tile is still in flight)
         const double *ts = tsum + h * G * kHD + j;
         const int64_t tend = CAUSAL ? g + 1 : G;
-        for (int64_t t = 0; t < tend; ++t) ks += ts[t * kHD];
+        for (int64_t t0 = 0; t0 < tend; t0 += 16) {
+            double x[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) x[u] = (t0 + u < tend) ? ts[(t0 + u) * kHD] : 0.0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (t0 + u < tend) ks += x[u];
+        }
     }
+    tile_store<NCH>(qt, j, v);
     __syncthreads();
     const double qa = sumsq_tile(qt, j, (int)((L - g * kQB < kQB) ? (L - g * kQB) : kQB));
     const double kn = USE_K ? __builtin_sqrt(ks) : 1.0;

@@ -462,15 +462,14 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
 }
 
 // ------------------------------------------------------------------ one wave per group
-// Used when there are many groups.  For K <= 64 * 128 one wave holds a whole
-// group: key i = 64 j + lane sits in
-// register j of lane `lane`, so loads coalesce and the kept indices, taken
-// in (j, lane) order, come out ascending.  Same steps as above without any
-// workgroup barrier: bit-pattern histogram in LDS, the bucket holding the
-// kk-th largest key by a wave prefix scan, T by exact rank among that
-// bucket's keys (at most 64 of them; otherwise a 2-bit search over all keys),
-// then the ordered compaction with ballots (keys == T kept in index order
-// until kk).
+// Used for many short groups (at most 64 * KPT <= 256 keys: the QK feature
+// lists of 128 candidates).  Key i = 64 j + lane sits in register j of lane
+// `lane`, so loads coalesce and the kept indices, taken in (j, lane) order,
+// come out ascending.  T by a bitwise search over the keys in registers, two
+// bits per round with ballot counts (a histogram and bucket scan over 2048
+// buckets took 7 us for 1024 groups of 128, ranking every key against every
+// other 10.9 us), then the ordered compaction with ballots (keys == T kept in
+// index order until kk).
 __device__ __forceinline__ int wave_min(int v)
 {
 #pragma unroll
@@ -501,8 +500,7 @@ __global__ void __launch_bounds__(64)
 k_select_wave(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__ idx, int64_t ldidx,
               float *__restrict__ thresh, double *__restrict__ bound)
 {
-    __shared__ uint32_t hist[kBuckets];
-    __shared__ int32_t cand[64];
+    static_assert(KPT <= 4, "one wave holds at most 256 keys");
     const int64_t grp = blockIdx.x;
     int64_t K, kk;
     if (sh.pv) {
@@ -535,99 +533,29 @@ k_select_wave(const float *__restrict__ scores, SelectShape sh, int32_t *__restr
     if (lo == hi) {
         T = lo;   // every key equal
     } else {
-        // ---- 1. histogram, bucket of the kk-th largest key
-        for (int b = lane; b < kBuckets; b += 64) hist[b] = 0;
-        wave_lds_sync();
-        const float scale = (float)kBuckets / (float)(hi - lo);
-        auto bucket = [&](int32_t k) -> int {
-            const int b = (int)((float)(k - lo) * scale);
-            return b < kBuckets - 1 ? b : kBuckets - 1;
-        };
-#pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            if (key[j] >= 0) atomicAdd(&hist[bucket(key[j])], 1u);
-        wave_lds_sync();
-        // lane l owns buckets 32 l .. 32 l + 31
-        uint32_t hb[32], mine = 0;
-#pragma unroll
-        for (int b = 0; b < 32; ++b) {
-            hb[b] = hist[32 * lane + b];
-            mine += hb[b];
-        }
-        // keys in the buckets of higher lanes
-        uint32_t incl = mine;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t x = __shfl_down(incl, d, 64);
-            if (lane + d < 64) incl += x;
-        }
-        int64_t cum = (int64_t)(incl - mine);
-        int bin = -1;
-        int64_t need = 0;
-#pragma unroll
-        for (int b = 31; b >= 0; --b) {
-            if (bin < 0 && cum < kk && kk <= cum + (int64_t)hb[b]) {
-                bin = 32 * lane + b;
-                need = kk - cum;
-            }
-            cum += hb[b];
-        }
-        const uint64_t who = __ballot(bin >= 0);
-        const int src = __builtin_ctzll(who);
-        bin = __shfl(bin, src, 64);
-        need = __shfl(need, src, 64);
-
-        // ---- 2. T among the bucket's keys
-        uint32_t nc = 0;
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) nc += (key[j] >= 0 && bucket(key[j]) == bin);
-        const uint32_t n1 = wave_sum(nc);
-        if (n1 <= 64) {
-            // compact the candidates into cand[0 .. n1)
-            uint32_t pos = 0;
+        // T = the largest value with #(keys >= T) >= kk, i.e. the kk-th
+        // largest key.  lo <= T <= hi, so T shares their common high bits;
+        // the rest are found two per round, counting the keys at or above
+        // three candidate prefixes with ballots (absent keys, -1, never count)
+        const int hb = 31 - __clz(lo ^ hi);
+        T = lo & ~((int32_t)((2u << hb) - 1u));
+        int b = hb;
+        for (; b >= 1; b -= 2) {
+            const int32_t c1 = T | (1 << (b - 1)), c2 = T | (2 << (b - 1)), c3 = T | (3 << (b - 1));
+            int64_t m1 = 0, m2 = 0, m3 = 0;
 #pragma unroll
             for (int j = 0; j < KPT; ++j) {
-                const bool in = key[j] >= 0 && bucket(key[j]) == bin;
-                const uint64_t m = __ballot(in);
-                if (in) cand[pos + __popcll(m & below)] = key[j];
-                pos += __popcll(m);
+                m1 += __popcll(__ballot(key[j] >= c1));
+                m2 += __popcll(__ballot(key[j] >= c2));
+                m3 += __popcll(__ballot(key[j] >= c3));
             }
-            wave_lds_sync();
-            const int32_t mineK = lane < (int)n1 ? cand[lane] : -1;
-            uint32_t gt = 0, ge = 0;
-            for (uint32_t i = 0; i < n1; ++i) {
-                const int32_t x = cand[i];
-                gt += x > mineK;
-                ge += x >= mineK;
-            }
-            const uint64_t hit = __ballot(lane < (int)n1 && gt < need && need <= ge);
-            T = __shfl(mineK, __builtin_ctzll(hit), 64);
-        } else {
-            // many keys in one bucket: 2-bit search over all keys, starting
-            // below the high bits lo and hi share
-            const int hb2 = 31 - __clz(lo ^ hi);
-            T = lo & ~((int32_t)((2u << hb2) - 1u));
-            int b = hb2;
-            for (; b >= 1; b -= 2) {
-                const int32_t c1 = T | (1 << (b - 1)), c2 = T | (2 << (b - 1)), c3 = T | (3 << (b - 1));
-                uint32_t m1 = 0, m2 = 0, m3 = 0;
+            T |= ((m3 >= kk) ? 3 : (m2 >= kk) ? 2 : (m1 >= kk) ? 1 : 0) << (b - 1);
+        }
+        if (b == 0) {
+            int64_t m1 = 0;
 #pragma unroll
-                for (int j = 0; j < KPT; ++j) {
-                    m1 += key[j] >= c1;
-                    m2 += key[j] >= c2;
-                    m3 += key[j] >= c3;
-                }
-                m1 = wave_sum(m1);
-                m2 = wave_sum(m2);
-                m3 = wave_sum(m3);
-                T |= ((m3 >= kk) ? 3 : (m2 >= kk) ? 2 : (m1 >= kk) ? 1 : 0) << (b - 1);
-            }
-            if (b == 0) {
-                uint32_t m1 = 0;
-#pragma unroll
-                for (int j = 0; j < KPT; ++j) m1 += key[j] >= (T | 1);
-                if ((int64_t)wave_sum(m1) >= kk) T |= 1;
-            }
+            for (int j = 0; j < KPT; ++j) m1 += __popcll(__ballot(key[j] >= (T | 1)));
+            if (m1 >= kk) T |= 1;
         }
     }
 
