@@ -451,8 +451,10 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                 }
             }
             if (u - 1 >= T) {
-                // the P tile of step u-1: with key scores, waves 4, 5 sum its key
-                // rows and waves 6, 7 store it; without, all four store it
+                // the P tile of step u-1: every helper lane stores an eighth of
+                // it; with key scores, lanes 2k and 2k+1 first sum half of key
+                // row k each (one helper wave per SIMD, so the summing does not
+                // pile onto two of the compute waves' SIMDs)
                 const uint16_t *pb = pbuf[(u - 1) & 1];
                 const int64_t kp0 = (int64_t)(u - 1 - T) * kKT;
                 auto store_tile = [&](int first, int stride, int n) {
@@ -466,28 +468,27 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                                                         (u32x4 *)(Pt + (h * L + k) * L + q0 + 8 * qc));
                     }
                 };
-                if (!PVS) {
-                    store_tile(ht, 256, 8);
-                } else if (ht < 128) {
-                    const int64_t k = kp0 + ht;
+                if (PVS) {
+                    // eight partial sums (query q mod 8), each in ascending q,
+                    // added as ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)):
+                    // lane 2k forms the first bracket, lane 2k+1 the second
+                    const int kr = ht >> 1, hf = ht & 1;
+                    const int64_t k = kp0 + kr;
+                    double m[4] = {0.0, 0.0, 0.0, 0.0};
                     if (k < Kvalid) {
-                        // eight partial sums (query mod 8), each in ascending q,
-                        // added pairwise: the chain is nq/8 adds long, not nq
-                        double m[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
                         for (int c = 0; c < nq / 8; ++c) {
-                            const u32x4 v = *(const u32x4 *)&pb[ht * kPitch + 8 * c];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                m[2 * e] += (double)bf16_lo(v[e]);
-                                m[2 * e + 1] += (double)bf16_hi(v[e]);
-                            }
+                            const u32x2 v = *(const u32x2 *)&pb[kr * kPitch + 8 * c + 4 * hf];
+                            m[0] += (double)bf16_lo(v[0]);
+                            m[1] += (double)bf16_hi(v[0]);
+                            m[2] += (double)bf16_lo(v[1]);
+                            m[3] += (double)bf16_hi(v[1]);
                         }
-                        const double mass = ((m[0] + m[1]) + (m[2] + m[3])) + ((m[4] + m[5]) + (m[6] + m[7]));
-                        pvs[(h * G + g) * L + k] = (float)(mass * vnorm[h * L + k]);
                     }
-                } else {
-                    store_tile(ht - 128, 128, 16);
+                    const double part = (m[0] + m[1]) + (m[2] + m[3]);
+                    const double other = __shfl_xor(part, 1, 64);
+                    if (hf == 0 && k < Kvalid) pvs[(h * G + g) * L + k] = (float)((part + other) * vnorm[h * L + k]);
                 }
+                store_tile(ht, 256, 8);
             }
             if (u < U) __syncthreads();
         }
