@@ -26,18 +26,19 @@
 // last slab is peeled off so the boundary is unconditional (the compiler's
 // waits before the last k-step's MFMAs then cover only that step's own reads).
 //
-// Pipeline (NS ring stages of BK-deep slabs; IDX(s) = DMA of slab s's kept
-// row indices into a per-wave LDS ring, AB(s) = the DMA loads of slab s's A
-// and B tiles):
+// Pipeline (NS ring stages of BK-deep slabs; IDX(s) = DMA of the kept row
+// indices of slabs s .. s+ICH-1 into a per-wave LDS ring, issued only where s
+// is a multiple of ICH; AB(s) = the DMA loads of slab s's A and B tiles):
 //   prologue   IDX(0 .. NS-1), wait; then IDX(p + NS), AB(p) for p < NS
-//   slab j     read the ring for AB(j+NS)'s rows (its index slab landed
+//   slab j     read the ring for AB(j+NS)'s rows (their index chunk landed
 //              with AB(j)), then the k-steps of slab j
 //   boundary j wait for AB(j+1); barrier; the first fragments of slab j+1;
 //              IDX(j + 2NS), AB(j + NS) into the stage slab j left
 // AB(s) is issued NS-1 slabs before it is used.  While every AB(j+2 ..
-// j+NS-1) has been issued, exactly (NS-2) pairs of operations are newer than
-// AB(j+1), so one constant wait count holds; near the end (nothing past the
-// last slab is loaded) the wait is for everything.
+// j+NS-1) has been issued, at least (NS-2) AB groups are newer than AB(j+1)
+// (an index chunk among them only makes the wait stricter), so one constant
+// wait count holds; near the end (nothing past the last slab is loaded) the
+// wait is for everything.
 //
 // Layouts (16-byte chunks, XOR-swizzled so every access pattern is free of
 // bank conflicts):
@@ -73,8 +74,9 @@ struct WtShape {
     static constexpr int B_DMA = B_BYTES / 1024 / NW;
     static constexpr int A_ROWS = 1024 / (BK * 2);          // A rows per DMA block
     static constexpr int B_ROWS = 1024 / (TN * 2);          // B rows per DMA block
-    static constexpr int IR = 2 * NS;                       // index ring slots (slab s: issue to use)
+    static constexpr int ICH = 256 / BK;                    // slabs per index chunk (one 16-byte DMA per lane)
     static_assert(KS % 2 == 0, "two register sets alternate over an even number of k-steps");
+    static_assert(2 * NS <= ICH, "an index chunk is issued before its first slab's rows are read");
     static_assert(B_ROWS == 2 && A_DMA >= 1 && B_DMA >= 1, "DMA blocks divide the tiles, two B rows each");
     
 };
@@ -88,9 +90,9 @@ k_gemm_wt(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
     using S = WtShape<TN, BK, NS>;
     constexpr int TM = S::TM, WN = S::WN, FM = S::FM, FN = S::FN, KS = S::KS;
     constexpr int AB_OPS = S::A_DMA + S::B_DMA;
-    constexpr int STEADY = (NS - 2) * ((IDX ? 1 : 0) + AB_OPS);
+    constexpr int STEADY = (NS - 2) * AB_OPS;   // index chunks not counted: waiting for more is safe
     __shared__ __attribute__((aligned(1024))) char smem[NS * S::STAGE];
-    __shared__ __attribute__((aligned(256))) int32_t iring[S::NW][S::IR][64];
+    __shared__ __attribute__((aligned(1024))) int32_t iring[S::NW][2][256];
 
     // ---- tile (XCD-aware: workgroup w runs on XCD w % 8, which takes a
     // contiguous range of tiles, N strip major, so an XCD's L2 holds one strip
@@ -131,12 +133,23 @@ k_gemm_wt(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
     const uint32_t smem0 = lds_addr(smem);
     const uint32_t iring0 = lds_addr(&iring[wave][0][0]);
 
-    // index entries of slab s into ring slot s % IR (lane l: entry l % BK;
-    // slabs past the end re-read slab 0, in bounds and never used)
+    // The kept-row indices of ICH slabs (256 entries) arrive by one 16-byte
+    // DMA per lane into a two-chunk ring per wave.  (One 4-byte DMA per slab
+    // cost as much as a 1 KiB one: this loop is bound by the DMA instructions a
+    // CU issues, about 34 cycles each, and it was the seventh of seven per
+    // slab.)  Chunk c is issued with the index slab s = ICH c, i.e. in the
+    // same step as, and before, AB(s - NS), which every wave has waited for
+    // before it reads row indices of slab s; chunk c + 2 reuses the slot after
+    // chunk c's last read.  Lanes past the index row re-read its last four
+    // entries (ldidx % 4 == 0): only entries below kk are ever used.
     auto issue_idx = [&](int s) {
         if constexpr (IDX) {
-            const int64_t j = (int64_t)(s < nkt ? s : 0) * BK + (lane % BK);
-            dma4(I + j, iring0 + (s % S::IR) * 256);
+            if (s % S::ICH == 0 && s < nkt) {
+                const int c = s / S::ICH;
+                int64_t off = (int64_t)c * 256 + 4 * lane;
+                if (off > ldidx - 4) off = ldidx - 4;
+                dma16(I + off, iring0 + (c & 1) * 1024);
+            }
         }
     };
     // sources of slab s's B rows for this wave's DMA blocks (rows past kk read
@@ -149,7 +162,7 @@ k_gemm_wt(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
 #pragma unroll
         for (int i = 0; i < S::B_DMA; ++i) {
             const int jr = (wave * S::B_DMA + i) * S::B_ROWS + lane / S::CB;
-            if constexpr (IDX) kr[i] = iring[wave][s % S::IR][jr];
+            if constexpr (IDX) kr[i] = iring[wave][(s / S::ICH) & 1][(s % S::ICH) * BK + jr];
             else kr[i] = (int32_t)(kbase + jr);
         }
     };
@@ -248,7 +261,7 @@ k_gemm_wt(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
         }
     }
     // slab 0 in LDS for every wave
-    if (nkt >= NS) vmwait<(NS - 1) * ((IDX ? 1 : 0) + AB_OPS)>();
+    if (nkt >= NS) vmwait<(NS - 1) * AB_OPS>();
     else vmwait<0>();
     clear_tail(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -258,18 +271,25 @@ k_gemm_wt(const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restric
     // compiler's waits before the last k-step's MFMAs cover only that step's
     // own fragments
     for (int j = 0; j + 1 < nkt; ++j) {
-        // the kept rows of AB(j+NS): its index slab landed with AB(j)
+        // the kept rows of AB(j+NS): its index chunk landed with AB(j).  Read
+        // on every step, also past the end (an in-bounds ring slot whose
+        // values are not used): with the reads under a branch, the compiler's
+        // merged wait before this slab's second MFMA covered them too, one LDS
+        // round trip per slab (1.06 against 0.96 us a slab at kk = K)
         const bool more = j + NS < nkt;
-        if (more) load_rows(j + NS);
+        load_rows(j + NS);
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
             read_frags(j, ks + 1, (ks & 1) ^ 1);
             mfmas(ks & 1);
         }
+        // the B row addresses of AB(j+NS) (a 64-bit product per row), formed
+        // while those MFMAs run rather than between the wait and the barrier
+        // below, where every wave of both workgroups on the CU waits for them
+        if (more) prep_b(j + NS);
         // boundary j: slab j+1 landed for this wave
         if (j + NS < nkt + 1) vmwait<STEADY>();
         else vmwait<0>();
-        if (more) prep_b(j + NS);
         clear_tail(j + 1);
         // every wave is done reading slab j and has slab j+1
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
