@@ -22,6 +22,11 @@ use the same contract; decode_q8 is the decode shape on the int8 weight path;
 attn4k and attn16k the attention chain (feature scores and selection,
 probabilities producer with the P.V key scores, key selection, reduced P.V).
 
+Every timed pass (whole steps, the per-stage pass, the GEMM back to back, the
+cold step) first runs its own work untimed for --settle-ms (30 ms) of GPU time,
+then its --warmup steps, then exactly --steps timed steps: after any idle spell
+the clocks need about 10 ms of work to reach their steady state.
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 import argparse
@@ -50,6 +55,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--settle-ms", type=float, default=30.0,
+                   help="untimed GPU work (ms) each timed pass runs first, so it sees steady-state clocks")
     p.add_argument("--workload", default="mlp_down",
                    choices=["attn_proj", "mlp_down", "decode", "decode_q8", "pv4k", "pv16k", "attn4k", "attn16k",
                             "tiny"])
@@ -491,10 +498,37 @@ def torch_int16(torch):
 
 
 # ------------------------------------------------------------------ timing
+SETTLE_MS = 30.0   # --settle-ms
+
+
+def settle(torch, fn):
+    """Run `fn` untimed until the GPU has been busy with it for SETTLE_MS.
+    After an idle spell (input generation, a CPU baseline, another pass's
+    synchronisation) the clocks take about 10 ms of work to ramp up: the
+    mlp_down r = 0.5 step measured 362 us over its first 20 steps, 328 over
+    the next 20 and 302-311 from then on, and 352 again after 0.5 s idle.  So
+    every timed pass first settles on its own work, then runs its warmup
+    steps, then its timed steps."""
+    if SETTLE_MS <= 0:
+        return
+    s = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    while True:
+        for _ in range(4):
+            fn()
+        b = torch.cuda.Event(enable_timing=True)
+        b.record(s)
+        b.synchronize()
+        if a.elapsed_time(b) >= SETTLE_MS:
+            return
+
+
 def back_to_back(torch, fn, steps, warmup):
     """ms per launch of `fn` run `steps` times back to back between two events
-    on the launch stream, after `warmup` untimed runs: the kernel's duration
-    plus the small gap between queued launches."""
+    on the launch stream, after the settling runs and `warmup` untimed runs:
+    the kernel's duration plus the small gap between queued launches."""
+    settle(torch, fn)
     for _ in range(warmup):
         fn()
     s = torch.cuda.current_stream()
@@ -514,9 +548,12 @@ def time_stages(torch, stages, steps, warmup, b2b):
     `steps` launches of the roofline kernel's call `b2b` back to back (events
     around a single launch would add its launch latency).  Returns
     (ms_per_step, {stage: mean ms}, ms per back-to-back launch)."""
-    for _ in range(warmup):
+    def one():
         for _, fn in stages:
             fn()
+    settle(torch, one)
+    for _ in range(warmup):
+        one()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -801,7 +838,9 @@ def run_oracle_pass(name, r, workers):
 
 
 def main():
+    global SETTLE_MS
     args = parse()
+    SETTLE_MS = args.settle_ms
     if args.oracle_pass:
         oracle_pass(args.oracle_pass)
         return
@@ -889,6 +928,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(h["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
