@@ -10,11 +10,11 @@
 // non-negative binary32, so their bit patterns, read as int32, order like the
 // values.  The threshold T (the kk-th largest key) is found in two steps:
 //   1. Bit-pattern histogram: with lo, hi the group's smallest and largest
-//      key, key u goes to bucket floor((u - lo) * 2048 / (hi - lo)), clamped
-//      to 2047, computed in binary32.  Conversion, multiplication by a
-//      positive constant and truncation are monotone, so the bucket index
-//      never decreases as u grows and equal keys share a bucket: the kk-th
-//      largest key lies in the bucket where the count from the top reaches kk.
+//      key, key u goes to bucket (u - lo) >> b, 2^b the narrowest power-of-two
+//      width for which 2048 buckets cover hi - lo.  The shift is monotone, so
+//      the bucket index never decreases as u grows and equal keys share a
+//      bucket: the kk-th largest key lies in the bucket where the count from
+//      the top reaches kk.
 //      Buckets even in the bit pattern are roughly even in log(score), so
 //      outlier channels do not crowd the bulk of the scores into a few
 //      buckets; the LDS atomics rarely collide and the threshold's bucket
@@ -27,9 +27,9 @@
 //      between them).  Every wave does this on its own, with the candidates
 //      in registers, so no barrier broadcasts T; beyond 1024 candidates all
 //      16 waves share the search through LDS.
-// Then the ordered compaction: per-wave exclusive counts of keys > T and == T
-// come from ballots masked to the lower lanes, per-wave totals from one LDS
-// exchange; keys == T are kept in index order until kk.  Atomics only place
+// Then the ordered compaction: each thread counts its keys > T and == T, a
+// prefix sum over the wave and one LDS exchange of the wave totals place its
+// kept keys; keys == T are kept in index order until kk.  Atomics only place
 // the candidates in LDS, whose order T does not depend on; no atomic decides
 // an output order and no floating-point sum decides anything, so the output
 // is deterministic.
@@ -68,21 +68,26 @@ __device__ __forceinline__ uint64_t block_sum_uniform(uint64_t v, uint64_t *slot
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
 
-// Exclusive prefix sum of a per-thread value v < 2^16 over the workgroup of
-// NW waves (thread order), plus the total.  Uses ballots on the bits of v.
+// Inclusive prefix sum over the 64 lanes of a wave, in six cross-lane steps
+// (a 16-ballot bit-sliced scan cost about ten times the vector instructions).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(v, d, 64);
+        if (lane >= d) v += y;
+    }
+    return v;
+}
+
+// Exclusive prefix sum of a per-thread value over the workgroup of NW waves
+// (thread order), plus the total (which must fit 32 bits).
 template <int NW>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wtot, uint32_t &total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint64_t below = lanes_below(lane);
-    uint32_t mine = 0, wsum = 0;
-#pragma unroll
-    for (int b = 0; b < 16; ++b) {
-        const uint64_t m = __ballot((v >> b) & 1u);
-        mine += (uint32_t)__popcll(m & below) << b;
-        wsum += (uint32_t)__popcll(m) << b;
-    }
-    if (lane == 0) wtot[wave] = wsum;
+    const uint32_t incl = wave_incl_scan(v, lane);
+    if (lane == 63) wtot[wave] = incl;
     __syncthreads();
     uint32_t before = 0;
     total = 0;
@@ -92,7 +97,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wtot, 
         before += (w < wave) ? x : 0;
         total += x;
     }
-    return before + mine;
+    return before + incl - v;
 }
 
 // Count of candidates >= c1, c2, c3 among cand[i], i in [first, n) step
@@ -143,7 +148,7 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     __shared__ uint32_t wtot[NW];
     __shared__ int32_t imin[NW], imax[NW];
     __shared__ double fsum[NW];
-    __shared__ int32_t s_last, s_bin;
+    __shared__ int32_t s_bin;
     __shared__ uint32_t s_nc;
     __shared__ int64_t s_above;
 
@@ -170,19 +175,21 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     const int64_t base = (int64_t)tid * kpt;
 
     for (int i = tid; i < kBuckets; i += NT) hist[i] = 0;
-    if (tid == 0) {
-        s_last = 0;   // written again (by the kk-th keeper) after several barriers
-        s_nc = 0;     // candidate count, first added to after two barriers
-    }
+    if (tid == 0) s_nc = 0;   // candidate count, first added to after two barriers
     int32_t key[KPT];           // -1 marks "no key here"; real keys are >= 0
     int32_t lo = 0x7fffffff, hi = 0;
     if (KPT % 4 == 0 && kpt == KPT && base + KPT <= K && ((uintptr_t)(s + base) & 15u) == 0) {
-        // a full, aligned run of keys: 16-byte loads
+        // a full, aligned run of keys: 16-byte loads, every key present
 #pragma unroll
         for (int i = 0; i < KPT; i += 4) {
             const u32x4 v = *(const u32x4 *)(s + base + i);
 #pragma unroll
             for (int e = 0; e < 4; ++e) key[i + e] = (int32_t)v[e];
+        }
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            lo = min(lo, key[i]);
+            hi = max(hi, key[i]);
         }
     } else {
 #pragma unroll
@@ -190,12 +197,12 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
             const int64_t k = base + i;
             key[i] = (i < kpt && k < K) ? __float_as_int(s[k]) : -1;
         }
-    }
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        if (key[i] >= 0) {
-            lo = min(lo, key[i]);
-            hi = max(hi, key[i]);
+        for (int i = 0; i < KPT; ++i) {
+            if (key[i] >= 0) {
+                lo = min(lo, key[i]);
+                hi = max(hi, key[i]);
+            }
         }
     }
     // ---- group min / max of the keys
@@ -214,11 +221,13 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         lo = min(lo, imin[w]);
         hi = max(hi, imax[w]);
     }
-    const float scale = (hi > lo) ? (float)kBuckets / (float)(hi - lo) : 0.0f;
-    auto bucket = [&](int32_t k) -> int {
-        const int b = (int)((float)(k - lo) * scale);
-        return b < kBuckets - 1 ? b : kBuckets - 1;
-    };
+    // buckets 2^bsh bit patterns wide, the narrowest power of two that covers
+    // hi - lo with kBuckets of them
+    const uint32_t span = hi > lo ? (uint32_t)(hi - lo) : 0u;
+    const int bits = span ? 32 - __clz(span) : 0;
+    const int bsh = bits > 11 ? bits - 11 : 0;
+    static_assert(kBuckets == 2048, "bucket widths assume 2^11 buckets");
+    auto bucket = [&](int32_t k) -> int { return (int)((uint32_t)(k - lo) >> bsh); };
 
     // ---- 1. bit-pattern histogram, then the bucket holding the kk-th key
 #pragma unroll
@@ -280,9 +289,13 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
     // wave's places.  Then every wave finds T on its own (no broadcast
     // barrier), unless there are more than 1024 candidates.
     const uint64_t below = lanes_below(lane);
+    // key k is in the bucket iff 0 <= k - blo < 2^bsh; an absent key (-1) wraps
+    // to at least 2^31 as an unsigned difference
+    const int32_t blo = lo + (bin << bsh);
+    const uint32_t bw = 1u << bsh;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        const bool in = key[i] >= 0 && bucket(key[i]) == bin;
+        const bool in = (uint32_t)(key[i] - blo) < bw;
         const uint64_t m = __ballot(in);
         if (m) {
             uint32_t at = 0;
@@ -361,17 +374,15 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         if ((int64_t)(c & 0x1fffff) >= need) T |= 1;
     }
 
-    // ---- 3. ordered compaction
-    uint32_t gt_w = 0, eq_w = 0, gt_tot_w = 0, eq_tot_w = 0;
+    // ---- 3. ordered compaction: per-thread counts of keys > T and == T
+    // (packed 16 bits each: a wave holds at most 64 * 64 keys), their
+    // exclusive prefix over the wave, the wave totals through LDS
+    uint32_t cnt = 0;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const uint64_t bg = __ballot(key[i] > T), be = __ballot(key[i] == T);
-        gt_w += __popcll(bg & below);
-        eq_w += __popcll(be & below);
-        gt_tot_w += __popcll(bg);
-        eq_tot_w += __popcll(be);
-    }
-    if (lane == 0) wsum64[wave] = ((uint64_t)gt_tot_w << 32) | eq_tot_w;
+    for (int i = 0; i < KPT; ++i) cnt += (key[i] > T ? 1u : 0u) + (key[i] == T ? 0x10000u : 0u);
+    const uint32_t cincl = wave_incl_scan(cnt, lane);
+    const uint32_t gt_w = (cincl - cnt) & 0xffffu, eq_w = (cincl - cnt) >> 16;
+    if (lane == 63) wsum64[wave] = ((uint64_t)(cincl & 0xffffu) << 32) | (cincl >> 16);
     __syncthreads();
     uint64_t before = 0, total = 0;
 #pragma unroll
@@ -380,30 +391,32 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         before += (w < wave) ? x : 0;
         total += x;
     }
-    const int64_t gt_before = (int64_t)(before >> 32) + gt_w;
-    const int64_t eq_before = (int64_t)(before & 0xffffffffu) + eq_w;
-    const int64_t need_eq = kk - (int64_t)(total >> 32);  // >= 1 by the choice of T
-    int64_t pos = gt_before + (eq_before < need_eq ? eq_before : need_eq);
-    int64_t eq_seen = eq_before;
+    // group sizes fit 32 bits (K < 2^31)
+    const int32_t kk32 = (int32_t)kk;
+    const int32_t gt_before = (int32_t)(before >> 32) + (int32_t)gt_w;
+    const int32_t eq_before = (int32_t)(before & 0xffffffffu) + (int32_t)eq_w;
+    const int32_t need_eq = kk32 - (int32_t)(total >> 32);  // >= 1 by the choice of T
+    int32_t pos = gt_before + min(eq_before, need_eq);
+    int32_t eq_seen = eq_before;
+    const int32_t kbase = (int32_t)base;
     int32_t *out = idx + grp * ldidx;
     double dropped = 0.0;
+    const bool want_bound = bound != nullptr;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        if (key[i] < 0) continue;
-        const int32_t k = (int32_t)(base + i);
-        bool keep = key[i] > T;
-        if (key[i] == T) {
+        const int32_t kv = key[i];      // -1 (absent) is neither kept nor dropped
+        bool keep = kv > T;
+        if (kv == T) {
             keep = eq_seen < need_eq;
             ++eq_seen;
         }
         if (keep) {
             // the kept list goes to LDS (every reader of cand passed a barrier
             // since) and leaves in one coalesced copy after the last barrier
-            if (pos < kk) cand[pos] = k;   // always true when T is the kk-th key
-            if (pos == kk - 1) s_last = k;
+            if (pos < kk32) cand[pos] = kbase + i;   // always true when T is the kk-th key
             ++pos;
-        } else {
-            dropped += (double)__int_as_float(key[i]);
+        } else if (want_bound && kv >= 0) {
+            dropped += (double)__int_as_float(kv);
         }
     }
     if (lead && tid == 0 && thresh) thresh[grp] = __int_as_float(T);
@@ -413,14 +426,17 @@ k_select(const float *__restrict__ scores, SelectShape sh, int32_t *__restrict__
         if (lane == 0) fsum[wave] = dropped;
     }
     if constexpr (NRB > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's row blocks
-    // LDS-only barrier: the kept list, fsum and s_last are in LDS; the one
+    // LDS-only barrier: the kept list and fsum are in LDS; the one
     // global store issued so far (thresh) is read by no one here, so there is
     // no need to wait for it as __syncthreads would
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int64_t padded = pad_up(kk);
     if (lead) {
         for (int64_t j = tid; j < kk; j += NT) out[j] = cand[j];
-        for (int64_t j = kk + tid; j < padded; j += NT) out[j] = s_last;
+        if (padded > kk) {
+            const int32_t last = cand[kk - 1];   // kk >= 1 here
+            for (int64_t j = kk + tid; j < padded; j += NT) out[j] = last;
+        }
         if (bound && tid == 0) {
             double b = 0.0;
             for (int w = 0; w < NW; ++w) b += fsum[w];
