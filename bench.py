@@ -271,7 +271,7 @@ class Linear:
         if self.gr <= 64:
             return "rmm::k_gemm_sk"
         tiles = self.G * -(-min(self.gr, self.M) // 128) * -(-self.N // 256)
-        return "rmm::k_gemm_wt" if tiles >= 512 and not self.f32 else "rmm::k_gemm_dl"
+        return "rmm::k_gemm_wb" if tiles >= 512 and not self.f32 else "rmm::k_gemm_dl"
 
     def cpu_baseline(self, r, groups):
         """The oracle (single-threaded fp64 C) on `groups` row groups at ratio r:
@@ -590,7 +590,8 @@ def step_time(torch, stages, steps, warmup):
 # ------------------------------------------------------------------ HBM traffic
 # sources of the kernel the roofline is taken on, per workload family
 GEMM_SOURCES = {
-    "linear": ["rmm_gemm.hip", "rmm_gemm_dl.h", "rmm_gemm_sk.h", "rmm_gemm_wt.h", "rmm_tile.h", "rmm_internal.h"],
+    "linear": ["rmm_gemm.hip", "rmm_gemm_dl.h", "rmm_gemm_sk.h", "rmm_gemm_wt.h", "rmm_gemm_wb.h", "rmm_tile.h",
+               "rmm_internal.h"],
     "pv": ["rmm_pv.hip", "rmm_tile.h", "rmm_internal.h"],
     "q8": ["rmm_q8.hip", "rmm_gemm_dl.h", "rmm_tile.h", "rmm_internal.h"],
     "attn": ["rmm_attn.hip", "rmm_tile.h", "rmm_internal.h"],

@@ -19,8 +19,11 @@
 // group.
 //
 // Kernels, by shape:
-//   k_gemm_wt  128 x 256 tiles, 4 waves of 128 x 64, two workgroups per CU
-//              (groups of more than 64 rows, at least 512 tiles, bf16 output)
+//   k_gemm_wb  128 x 256 tiles, 4 waves of 128 x 64, two workgroups per CU,
+//              kept B rows straight into registers (an index list, groups of
+//              more than 64 rows, at least 512 tiles, bf16 output)
+//   k_gemm_wt  the same tiles with B through LDS by DMA (the dense product
+//              on those shapes)
 //   k_gemm_dl  128 x 256 tiles, 8 waves of 64 x 64 (other prefill shapes)
 //   k_gemm_sk  64 x 128 tiles streaming the kept rows (<= 64 rows per group,
 //              e.g. decode: many N tiles over the kept rows of a wide weight)
@@ -29,6 +32,7 @@
 #include "rmm_gemm_dl.h"
 #include "rmm_gemm_sk.h"
 #include "rmm_gemm_wt.h"
+#include "rmm_gemm_wb.h"
 
 #ifndef RMM_DL_WAVES
 #define RMM_DL_WAVES 8
@@ -194,9 +198,9 @@ static hipError_t launch_shape(const uint16_t *A, int64_t lda, const uint16_t *B
     return hipGetLastError();
 }
 
-// tiles from which the two-per-CU kernel runs: two per CU of the 256 CUs of an
+// tiles from which the two-per-CU kernels run: two per CU of the 256 CUs of an
 // MI355X (with fewer, a CU holds one workgroup and k_gemm_dl is faster)
-constexpr int64_t kWtMinTiles = 512;
+constexpr int64_t kTwoPerCuMinTiles = 512;
 
 hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                        const int32_t *idx, int64_t ldidx, int64_t M, int64_t N, int64_t kk,
@@ -205,21 +209,33 @@ hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_
     const int64_t rows = group_rows < M ? group_rows : M;
     const int64_t kslab = (kk + 63) / 64 * 64;
     // two 128 x 256 workgroups per CU when there are at least two tiles per
-    // CU (bf16 output; A byte offsets fit 32 bits)
+    // CU (bf16 output; A byte offsets fit 32 bits): with an index list the
+    // kept B rows go straight into registers (k_gemm_wb, which also needs a
+    // B row stride under 2^23 elements for its 24-bit offset multiply), the
+    // dense product streams B through LDS (k_gemm_wt); each measured the
+    // faster on its case
     if (rows > 64 && lda >= kslab && (!idx || ldidx >= kslab) && ydt == 1 && M * lda * 2 < (int64_t(1) << 32)) {
-        using S = WtShape<256, 32, 3>;
+        constexpr int TN = 256;
         const int64_t G = (M + group_rows - 1) / group_rows;
-        const int tpg = (int)((rows + S::TM - 1) / S::TM);
+        const int tpg = (int)((rows + 127) / 128);
         const int m_tiles = (int)(G * tpg);
-        const int n_tiles = (int)((N + S::TN - 1) / S::TN);
-        if ((int64_t)m_tiles * n_tiles >= kWtMinTiles) {
+        const int n_tiles = (int)((N + TN - 1) / TN);
+        if ((int64_t)m_tiles * n_tiles >= kTwoPerCuMinTiles) {
             const int per = (m_tiles * n_tiles + 7) / 8;
-            if (idx)
-                hipLaunchKernelGGL((k_gemm_wt<256, 32, 3, true>), dim3((unsigned)(8 * per)), dim3(256), 0, s, A, lda,
+            if (idx && ldb * 2 < (int64_t(1) << 24)) {
+                // the largest B row whose byte offset row * ldb * 2 + 2N fits 32 bits
+                int64_t lim = ((int64_t(1) << 32) - 1 - 2 * N) / (2 * ldb);
+                if (lim > (int64_t(1) << 24) - 1) lim = (int64_t(1) << 24) - 1;
+                hipLaunchKernelGGL((k_gemm_wb<4>), dim3((unsigned)(8 * per)), dim3(256), 0, s, A, lda, B, ldb, idx,
+                                   ldidx, M, N, kk, group_rows, (uint16_t *)Y, ldy, tpg, m_tiles, n_tiles,
+                                   (uint32_t)lim);
+            } else if (idx) {
+                hipLaunchKernelGGL((k_gemm_wt<TN, 32, 3, true>), dim3((unsigned)(8 * per)), dim3(256), 0, s, A, lda,
                                    B, ldb, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy, tpg, m_tiles, n_tiles);
-            else
-                hipLaunchKernelGGL((k_gemm_wt<256, 32, 3, false>), dim3((unsigned)(8 * per)), dim3(256), 0, s, A,
-                                   lda, B, ldb, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy, tpg, m_tiles, n_tiles);
+            } else {
+                hipLaunchKernelGGL((k_gemm_wt<TN, 32, 3, false>), dim3((unsigned)(8 * per)), dim3(256), 0, s, A, lda,
+                                   B, ldb, idx, ldidx, M, N, kk, group_rows, Y, ydt, ldy, tpg, m_tiles, n_tiles);
+            }
             return hipGetLastError();
         }
     }

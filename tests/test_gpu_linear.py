@@ -505,3 +505,31 @@ def test_two_per_cu_gemm(case):
     assert np.array_equal(down(Y), synth.f32_to_bf16_bits(down(Y32))), f"{tag}: bf16 output is not RNE(fp32 output)"
     Yref, Sabs = oracle_rows(c["A64"], c["B64"], ig, kk, gr, np.arange(M))
     check_output(widen(Y), Yref, Sabs, kk, tag)
+
+
+def test_two_per_cu_far_rows():
+    """Kept B rows more than 2^32 bytes past B's start (a 2 MiB row stride, so
+    rows from 2048 on): their 32-bit offsets do not hold, and the waves that
+    meet them recompute their part with 64-bit addresses.  The output equals,
+    bit for bit, that of the same product over a compact copy of B (the fast
+    path), and every group's sampled rows match the oracle."""
+    M, K, N, gr, r = 4096, 2304, 4096, 128, 0.5
+    ldb = 1 << 20
+    tag = f"far rows {M}x{K}x{N} ldb={ldb} r={r}"
+    log(f"case {tag}")
+    c = make_case("mlp_down", M, K, N, seed=35)
+    bnorm = rmm.rmm_rownorms(c["B"])
+    idx, scores, thresh, bound, Ap, Y = run_chain(c, r, gr, bnorm)
+    kk = rmm.rmm_kk(r, K)
+    far = ((1 << 32) - 1 - 2 * N) // (2 * ldb)
+    assert int(idx[:, :kk].max()) > far, "no kept row past the 32-bit offsets"
+    Bbig = torch.empty((K, ldb), dtype=torch.bfloat16, device=DEV)   # 4.8 GB, first N columns used
+    Bbig[:, :N] = c["B"]
+    Yfar = rmm.rmm_gemm(Ap, Bbig[:, :N], idx, kk, gr)
+    torch.cuda.synchronize()
+    assert torch.equal(Yfar, Y), f"{tag}: output differs from the compact-B product"
+    del Bbig
+    rows = group_rows_sample(M, gr)
+    ig = down(idx)[:, :kk]
+    Yref, Sabs = oracle_rows(c["A64"], c["B64"], ig, kk, gr, rows)
+    check_output(widen(Yfar)[rows], Yref, Sabs, kk, tag + f" ({len(rows)} rows: every group)")

@@ -112,6 +112,7 @@ NT_STREAMS = [
     ("rmm_q8.hip", "k_gemm_q8", "global_load_lds_dwordx4", True),
     ("rmm_gemm.hip", "k_gemm_dl", "global_store_dwordx4", False),
     ("rmm_gemm.hip", "k_gemm_wt", "global_store_dwordx4", True),
+    ("rmm_gemm.hip", "k_gemm_wb", "global_store_dwordx4", True),
     ("rmm_gather.hip", "k_gather_rows", "global_store_dwordx4", True),
     ("rmm_select.hip", "k_select", "global_store_dwordx4", False),
 ]
