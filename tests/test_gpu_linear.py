@@ -475,6 +475,9 @@ WT = [
     (4046, 1000, 4104, 128, 0.37),   # 32 groups, the last of 78 rows; N tail of 8; kk = 370
     (4046, 1000, 4104, 128, 1.0),    # the dense product, A and B in place
     (2048, 520, 8192, 256, 0.5),     # two row tiles per group; kk = 260 (ragged last slab)
+    (4096, 40, 4096, 128, 0.5),      # kk = 20: one partial slab, no main loop
+    (4096, 200, 4096, 128, 0.004),   # kk = 1
+    (4096, 1096, 4096, 128, 0.61),   # kk = 669: three index chunks, an odd slab count (21)
 ]
 
 
