@@ -14,8 +14,11 @@
 // each SIMD runs one wave of each.  A workgroup waits at its one barrier per
 // slab whenever its waves drift apart (measured: a third of the loop with one
 // workgroup per CU); with two, the other workgroup's MFMAs fill that time.
-// The launcher takes this kernel only when there are at least two tiles per
-// CU (the MLP down-projection: 32 groups x 16 strips), k_gemm_dl otherwise.
+// The launcher takes this kernel when there are at least two tiles per CU
+// (the MLP down-projection: 32 groups x 16 strips) for the dense product, and
+// with an index list only when B's row stride is too large for k_gemm_wb's
+// 24-bit offset multiply (k_gemm_wb, B straight into registers, is faster
+// with an index list and slower dense); k_gemm_dl with fewer tiles.
 //
 // The loop is software-pipelined: fragments of k-step s+1 are read into a
 // second register set before the MFMAs of step s are issued.  The slab
