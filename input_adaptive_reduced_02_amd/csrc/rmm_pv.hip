@@ -8,7 +8,8 @@
 // block needs from key k are one contiguous 256-byte segment, and V[h][k][:]
 // is another.  Both are fetched in place by kept-key index (no gather pass,
 // dropped keys are never read), straight from global memory into LDS by
-// 16-byte DMA, through a (D+1)-stage ring with D slabs of 64 keys in flight.
+// 16-byte DMA, through a (D+1)-stage ring with D slabs of 32 or 64 keys in
+// flight.
 //
 // Both operands arrive key-major, i.e. k-major rows of 256 B, and both MFMA
 // fragments (A: 32 queries x 16 keys, B: 16 keys x 32 d) come from the
@@ -37,9 +38,8 @@ namespace {
 
 constexpr int kPvD = 3;                 // slabs in flight
 constexpr int kPvStages = kPvD + 1;
-constexpr int kPvBK = 64;               // keys per slab
-constexpr int kPvTile = 128 * kPvBK;    // elements of one operand tile (16 KiB)
 constexpr int kPvIdxRing = 2 * kPvD;
+constexpr int kPvIdxSlot = 64;          // kept-key indices one 4-byte DMA brings (64 lanes)
 
 __device__ __forceinline__ int swz_pv(int k) { return (k & 3) << 2; }
 
@@ -81,18 +81,27 @@ __device__ __forceinline__ bf16x8 tr_frag(const char *p)
 
 }  // namespace
 
-template <bool IDX>
-__global__ void __launch_bounds__(256)
+// BK keys per slab: 64 (128 KiB of ring, one workgroup per CU) or 32 (64 KiB,
+// two per CU, so one workgroup's index wait, pipeline fill and epilogue
+// overlap the other's streaming).  Measured at H = 32 (same box, identical
+// outputs): L = 4096 r = 0.5 75.4 against 83.5 us, r = 1 129 against 131-135;
+// L = 16384 r = 0.5 915 against 924-930, r = 1 1740 against 1680 us -- the
+// short workgroups gain, the longest lose to the second barrier per 64 keys.
+template <bool IDX, int BK>
+__global__ void __launch_bounds__(256, 64 / BK)
 k_pv_gemm(const uint16_t *__restrict__ Pt, const uint16_t *__restrict__ V, int64_t H, int64_t L,
           int64_t Gq, int64_t qb, int causal, double r, const int32_t *__restrict__ idx, int64_t ldidx,
           void *__restrict__ O, int odt)
 {
-    constexpr int D = kPvD, BK = kPvBK, FM = 2, FN = 2;
-    constexpr int A_SHARE = 4, B_SHARE = 4;   // 1 KiB DMA blocks per wave per slab (P, V)
+    constexpr int D = kPvD, FM = 2, FN = 2;
+    constexpr int kPvTile = 128 * BK;          // elements of one operand tile (BK key rows)
+    constexpr int A_SHARE = BK / 16, B_SHARE = BK / 16;   // 1 KiB DMA blocks per wave per slab (P, V)
     constexpr int AB_OPS = A_SHARE + B_SHARE;
     constexpr int STEADY = (D - 1) * ((IDX ? 1 : 0) + AB_OPS);
+    // the bf16 epilogue stages the 128 x 128 output tile (34 KiB) in the ring
+    static_assert(kPvStages * 2 * kPvTile * 2 >= 128 * (128 * 2 + 16), "ring too small for the epilogue");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[kPvStages * 2 * kPvTile];
-    __shared__ __attribute__((aligned(256))) int32_t iring[4][kPvIdxRing][BK];
+    __shared__ __attribute__((aligned(256))) int32_t iring[4][kPvIdxRing][kPvIdxSlot];
 
     const int64_t b = blockIdx.x;
     const int64_t g = Gq - 1 - b / H;
@@ -124,10 +133,12 @@ k_pv_gemm(const uint16_t *__restrict__ Pt, const uint16_t *__restrict__ V, int64
     const uint32_t smem0 = pv_lds_addr(smem);
     const uint32_t iring0 = pv_lds_addr(&iring[wave][0][0]);
 
+    // the slab's BK indices (with BK = 32 lanes 32-63 repeat lanes 0-31, so no
+    // lane reads past the slab's end of the padded index row)
     auto issue_idx = [&](int kt) {
         if constexpr (IDX) {
-            const int64_t j = (int64_t)(kt < nkt ? kt : 0) * BK + lane;
-            pv_dma4(I + j, iring0 + (kt % kPvIdxRing) * BK * 4);
+            const int64_t j = (int64_t)(kt < nkt ? kt : 0) * BK + (lane & (BK - 1));
+            pv_dma4(I + j, iring0 + (kt % kPvIdxRing) * kPvIdxSlot * 4);
         }
     };
     auto issue_ab = [&](int kt) {
@@ -260,12 +271,24 @@ hipError_t launch_pv_gemm(const uint16_t *Pt, const uint16_t *V, int64_t H, int6
                           void *O, int odt, hipStream_t s)
 {
     const int64_t Gq = (L + qblock - 1) / qblock;
-    if (idx)
-        hipLaunchKernelGGL(k_pv_gemm<true>, dim3((unsigned)(H * Gq)), dim3(256), 0, s, Pt, V, H, L, Gq, qblock,
-                           causal, r, idx, ldidx, O, odt);
-    else
-        hipLaunchKernelGGL(k_pv_gemm<false>, dim3((unsigned)(H * Gq)), dim3(256), 0, s, Pt, V, H, L, Gq, qblock,
-                           causal, r, idx, ldidx, O, odt);
+    // 32-key slabs while the largest block keeps at most 8192 keys
+    const int64_t kk_max = idx ? kk_rule(r, L) : L;
+    const dim3 grid((unsigned)(H * Gq)), block(256);
+    if (kk_max <= 8192) {
+        if (idx)
+            hipLaunchKernelGGL((k_pv_gemm<true, 32>), grid, block, 0, s, Pt, V, H, L, Gq, qblock, causal, r, idx,
+                               ldidx, O, odt);
+        else
+            hipLaunchKernelGGL((k_pv_gemm<false, 32>), grid, block, 0, s, Pt, V, H, L, Gq, qblock, causal, r, idx,
+                               ldidx, O, odt);
+    } else {
+        if (idx)
+            hipLaunchKernelGGL((k_pv_gemm<true, 64>), grid, block, 0, s, Pt, V, H, L, Gq, qblock, causal, r, idx,
+                               ldidx, O, odt);
+        else
+            hipLaunchKernelGGL((k_pv_gemm<false, 64>), grid, block, 0, s, Pt, V, H, L, Gq, qblock, causal, r, idx,
+                               ldidx, O, odt);
+    }
     return hipGetLastError();
 }
 
