@@ -263,11 +263,17 @@ class Linear:
 
     @property
     def kernel(self):
-        """The kernel the reduced GEMM runs on: groups of at most 64 rows the
-        decode kernel; prefill shapes with at least 512 tiles of 128 x 256 and
-        bf16 output two workgroups per CU, other prefill shapes eight waves."""
+        return self.kernel_for(0.5)
+
+    def kernel_for(self, r):
+        """The kernel the reduced GEMM runs on at ratio r: int8 weights the
+        shared-stream kernel for groups of at most 64 rows keeping at most 4096
+        rows, else the split-tile one; groups of at most 64 rows the decode
+        kernel; prefill shapes with at least 512 tiles of 128 x 256 and bf16
+        output two workgroups per CU, other prefill shapes eight waves."""
         if self.q8:
-            return "rmm::k_gemm_q8"
+            kk = self.rmm.rmm_kk(r, self.K)
+            return "rmm::k_gemm_q8s" if self.gr <= 64 and kk <= 4096 else "rmm::k_gemm_q8"
         if self.gr <= 64:
             return "rmm::k_gemm_sk"
         tiles = self.G * -(-min(self.gr, self.M) // 128) * -(-self.N // 256)
@@ -719,7 +725,7 @@ def roofline(W, r, gemm_ms):
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4))
     roof["traffic"] = measured_traffic(W.name, r, getattr(W, "profile_prefix", "k_gemm"))
-    roof["kernel"] = W.kernel
+    roof["kernel"] = W.kernel_for(r) if hasattr(W, "kernel_for") else W.kernel
     roof["kernel_ms"] = round(gemm_ms, 5)
     return roof
 

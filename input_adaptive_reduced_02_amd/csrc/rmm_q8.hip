@@ -515,6 +515,207 @@ k_gemm_q8(const uint16_t *__restrict__ A, int64_t lda, const int8_t *__restrict_
     }
 }
 
+// ------------------------------------------------------------------ GEMM, short kept lists
+// k_gemm_q8s: for groups of at most 64 rows and at most 4096 kept rows.  One
+// workgroup per 64 x 128 tile; its 4 waves sit side by side along N (wave w:
+// columns 32w .. 32w+31, all 64 rows) and share one stream of 64-deep slabs
+// through a 4-stage DMA ring (3 slabs in flight), so there are no partial
+// sums to reduce and no split to hand off.  A short loop is where those fixed
+// costs of k_gemm_q8 weigh most: decode shape (64 x 8192 @ 8192 x 28672, same
+// box, identical outputs) 24.5 against 30.4 us at kk = 2458, 37.8 against
+// 39.6 us at kk = 4096; past that the per-slab widening and MFMAs no longer
+// hide under the stream (51.6 against 49.9 us at kk = 5735).
+struct Q8sShape {
+    static constexpr int TM = 64, TN = 128, BK = 64, NW = 4, WN = 32, FM = 2, KS = BK / 16;
+    static constexpr int D = 3, NSTAGE = D + 1, IDX_RING = 2 * D;
+    static constexpr int A_BYTES = TM * BK * 2, B_BYTES = BK * TN, STAGE = A_BYTES + B_BYTES;   // 8 + 8 KiB
+    static constexpr int A_SHARE = A_BYTES / 1024 / NW, B_SHARE = B_BYTES / 1024 / NW;       // 2, 2
+};
+
+// B rows of 128 bytes: chunk pair shifted by (k >> 1) & 3 (as swz_q8 for 128-byte rows)
+__device__ __forceinline__ int swz_q8s(int k) { return ((k >> 1) & 3) << 1; }
+
+template <bool IDX>
+__global__ void __launch_bounds__(256)
+k_gemm_q8s(const uint16_t *__restrict__ A, int64_t lda, const int8_t *__restrict__ Bq, int64_t ldq,
+           const float *__restrict__ scale, const int32_t *__restrict__ idx, int64_t ldidx, int64_t M, int64_t N,
+           int64_t kk, int64_t gr, void *__restrict__ Y, int ydt, int64_t ldy, int m_tiles, int n_tiles)
+{
+    using S = Q8sShape;
+    constexpr int BK = S::BK, TN = S::TN, WN = S::WN, FM = S::FM, KS = S::KS, D = S::D;
+    constexpr int AB_OPS = S::A_SHARE + S::B_SHARE;
+    constexpr int STEADY = (D - 1) * ((IDX ? 1 : 0) + AB_OPS);   // operations always newer than AB(i)
+    __shared__ __attribute__((aligned(1024))) char smem[S::NSTAGE * S::STAGE];
+    __shared__ __attribute__((aligned(256))) int32_t iring[S::NW][S::IDX_RING][BK];
+
+    // consecutive workgroups on consecutive XCDs take tiles 'per' apart
+    const int total = m_tiles * n_tiles;
+    const int per = (total + 7) / 8;
+    const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (t >= total) return;
+    const int nt = t / m_tiles, g = t % m_tiles;      // one row tile per group (gr <= 64)
+    const int64_t row0 = (int64_t)g * gr;
+    const int64_t row_end = (row0 + gr < M) ? row0 + gr : M;
+    const int64_t col0 = (int64_t)nt * TN;
+    const int32_t *I = IDX ? idx + g * ldidx : nullptr;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nkt = (int)((kk + BK - 1) / BK);
+
+    // per-lane DMA sources: A rows (rows past M copy row M-1; rows of the next
+    // group are loaded and never stored), B column chunks (past N: chunk 0)
+    const uint16_t *a_src[S::A_SHARE];
+#pragma unroll
+    for (int i = 0; i < S::A_SHARE; ++i) {
+        const int r = (wave * S::A_SHARE + i) * 8 + (lane >> 3);
+        int64_t row = row0 + r;
+        if (row > M - 1) row = M - 1;
+        a_src[i] = A + row * lda + (((lane & 7) ^ swz(r)) << 3);
+    }
+    const int8_t *b_src[S::B_SHARE];
+#pragma unroll
+    for (int i = 0; i < S::B_SHARE; ++i) {
+        const int k = (wave * S::B_SHARE + i) * 8 + (lane >> 3);
+        const int64_t c = col0 + (((lane & 7) ^ swz_q8s(k)) << 4);
+        b_src[i] = Bq + ((c < N) ? c : 0);
+    }
+    const uint32_t smem0 = lds_addr(smem);
+    const uint32_t iring0 = lds_addr(&iring[wave][0][0]);
+    // the slab's 64 kept-row indices (slabs past the end reload slab 0's)
+    auto issue_idx = [&](int kt) {
+        if constexpr (IDX) {
+            const int64_t j = (int64_t)(kt < nkt ? kt : 0) * BK + lane;
+            dma4(I + j, iring0 + (kt % S::IDX_RING) * BK * 4);
+        }
+    };
+    auto load_rows = [&](int kt, int32_t (&kr)[S::B_SHARE]) {
+#pragma unroll
+        for (int i = 0; i < S::B_SHARE; ++i) {
+            const int jr = (wave * S::B_SHARE + i) * 8 + (lane >> 3);
+            if constexpr (IDX) kr[i] = iring[wave][kt % S::IDX_RING][jr];
+            else kr[i] = kt * BK + jr;
+        }
+    };
+    // A and B of slab kt (past the end: the last A slab and B row 0, valid
+    // memory whose products are cleared in registers)
+    auto issue_ab = [&](int kt, const int32_t (&kr)[S::B_SHARE]) {
+        const int64_t kbase = (int64_t)kt * BK;
+        const int64_t abase = (int64_t)(kt < nkt ? kt : nkt - 1) * BK;
+        const uint32_t sa = smem0 + (kt % S::NSTAGE) * S::STAGE;
+        const uint32_t sb = sa + S::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < S::A_SHARE; ++i) dma16(a_src[i] + abase, sa + (wave * S::A_SHARE + i) * 1024);
+#pragma unroll
+        for (int i = 0; i < S::B_SHARE; ++i) {
+            const int jr = (wave * S::B_SHARE + i) * 8 + (lane >> 3);
+            const int64_t krow = (kbase + jr < kk) ? kr[i] : 0;
+            dma16_nt(b_src[i] + krow * ldq, sb + (wave * S::B_SHARE + i) * 1024);
+        }
+    };
+    // this lane's byte offset of its transposed B read within a stage
+    int b_off;
+    {
+        const int blk = lane >> 4, b = (lane & 15) >> 1, h = lane & 1;
+        const int k = (blk >> 1) * 8 + b;
+        b_off = S::A_BYTES + k * TN + (((2 * wave + (blk & 1)) ^ swz_q8s(k)) << 4) + h * 8;
+    }
+    floatx16 acc[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[fm][v] = 0.0f;
+
+#pragma unroll
+    for (int p = 0; p < D; ++p) issue_idx(p);
+    vmwait<0>();
+#pragma unroll
+    for (int p = 0; p < D; ++p) {
+        issue_idx(p + D);
+        int32_t kr[S::B_SHARE];
+        load_rows(p, kr);
+        issue_ab(p, kr);
+    }
+    for (int kt = 0; kt < nkt; ++kt) {
+        vmwait<STEADY>();   // this wave's share of slab kt landed
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        int32_t kr[S::B_SHARE];
+        load_rows(kt + D, kr);
+        const char *st = smem + (kt % S::NSTAGE) * S::STAGE;
+        const uint16_t *sa = (const uint16_t *)st;
+        u32x4 af[KS][FM];
+        intx2 bf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int c = 2 * ks + (lane >> 5);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int r = fm * 32 + (lane & 31);
+                af[ks][fm] = *(const u32x4 *)(sa + r * BK + ((c ^ swz(r)) << 3));
+            }
+            bf[ks] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2 *)(st + b_off + ks * 16 * TN));
+        }
+        issue_idx(kt + 2 * D);
+        issue_ab(kt + D, kr);
+        if ((int64_t)(kt + 1) * BK > kk) {   // partial last slab: clear A columns >= kk
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int64_t k0 = (int64_t)kt * BK + ks * 16 + 8 * (lane >> 5);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t m = (k0 + 2 * j < kk ? 0x0000ffffu : 0u) | (k0 + 2 * j + 1 < kk ? 0xffff0000u : 0u);
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) af[ks][fm][j] &= m;
+                }
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 b = q8_frag(bf[ks]);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[ks][fm]), b, acc[fm],
+                                                                  0, 0, 0);
+        }
+    }
+    vmwait<0>();   // the trailing reloads: no DMA may land after the workgroup ends
+
+    const int colw = wave * WN + acc_col(lane);
+    const float sc = (col0 + colw < N) ? scale[col0 + colw] : 0.0f;
+    if (ydt == 1) {
+        // bf16 output: stage the 64 x 128 tile in LDS (the ring is free once
+        // every wave has passed the barrier below), then 16-byte row chunks
+        constexpr int PITCH = TN * 2 + 16;
+        char *stg = smem;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = fm * 32 + acc_row(lane, v);
+                *(uint16_t *)(stg + r * PITCH + 2 * colw) = (uint16_t)f32_to_bf16(acc[fm][v] * sc);
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int e = threadIdx.x; e < S::TM * (TN / 8); e += 256) {
+            const int r = e / (TN / 8), ch = e % (TN / 8);
+            const int64_t row = row0 + r, cl = col0 + 8 * ch;
+            if (row < row_end && cl < N)
+                __builtin_nontemporal_store(*(const u32x4 *)(stg + r * PITCH + 16 * ch),
+                                            (u32x4 *)((uint16_t *)Y + row * ldy + cl));
+        }
+        return;
+    }
+    const int64_t col = col0 + colw;
+    if (col < N) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = row0 + fm * 32 + acc_row(lane, v);
+                if (row < row_end) ((float *)Y)[row * ldy + col] = acc[fm][v] * sc;
+            }
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 hipError_t launch_quantize_q8(const uint16_t *B, int64_t K, int64_t N, int64_t ldb, int8_t *q,
                               int64_t ldq, float *scale, hipStream_t s)
@@ -593,6 +794,20 @@ hipError_t launch_gemm_q8(const uint16_t *A, int64_t lda, const int8_t *Bq, int6
         arrivals = (unsigned int *)ws;
         const size_t off = (ws_bytes - q8_partial_bytes((int64_t)m_tiles * n_tiles)) / 256 * 256;
         part_ws = (float *)((char *)ws + off);
+    }
+    // short kept lists of small groups: one shared slab stream per 64 x 128
+    // tile (its loads read whole 64-deep slabs of the panel and the index row)
+    if (group_rows <= 64 && kk <= 4096 && lda >= pad_up(kk) && (!idx || ldidx >= pad_up(kk))) {
+        using T = Q8sShape;
+        const int mt = (int)G, ntl = (int)((N + T::TN - 1) / T::TN);
+        const dim3 g8((unsigned)(8 * ((mt * ntl + 7) / 8))), b8(64 * T::NW);
+        if (idx)
+            hipLaunchKernelGGL(k_gemm_q8s<true>, g8, b8, 0, s, A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk,
+                               group_rows, Y, ydt, ldy, mt, ntl);
+        else
+            hipLaunchKernelGGL(k_gemm_q8s<false>, g8, b8, 0, s, A, lda, Bq, ldq, scale, idx, ldidx, M, N, kk,
+                               group_rows, Y, ydt, ldy, mt, ntl);
+        return hipGetLastError();
     }
     const dim3 grid((unsigned)(8 * ((total + 7) / 8))), block(64 * S::NW);
     if (idx)

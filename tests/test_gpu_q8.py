@@ -106,14 +106,18 @@ def check_chain(A64, Bd, b_ref, idx, scores, Y, r, gr, tag, rows=None):
 
 
 SMALL = [
-    # (M, K, N, group_rows, r)
-    (64, 4096, 1024, 64, 0.3),       # decode-like: one group, kk = 1229
-    (300, 1000, 272, 128, 0.5),      # groups 128,128,44 (3 row tiles each); N tail 16
-    (200, 520, 80, 128, 0.37),       # kk = 193, N = 80 (one partial column tile)
-    (96, 136, 48, 32, 0.9),          # groups of 32 rows: half-empty row tiles, kk = 123
-    (128, 512, 256, 64, 1.0),        # the dense product, same kernel, no index list
-    (64, 8, 16, 64, 0.1),            # kk = 1
-    (16, 96, 32, 1, 0.25),           # one-row groups
+    # (M, K, N, group_rows, r); groups of at most 64 rows keeping at most 4096
+    # rows run the shared-stream kernel (q8s), the others the split-tile one
+    (64, 4096, 1024, 64, 0.3),       # q8s, decode-like: one group, kk = 1229
+    (300, 1000, 272, 128, 0.5),      # split: groups 128,128,44 (3 row tiles each); N tail 16
+    (200, 520, 80, 128, 0.37),       # split: kk = 193, N = 80 (one partial column tile)
+    (96, 136, 48, 32, 0.9),          # q8s: groups of 32 rows (half-empty row tiles), kk = 123
+    (128, 512, 256, 64, 1.0),        # q8s: the dense product, no index list, also binary32 out
+    (256, 384, 272, 128, 1.0),       # split: the dense product, also binary32 out
+    (64, 8, 16, 64, 0.1),            # q8s: kk = 1
+    (16, 96, 32, 1, 0.25),           # q8s: one-row groups
+    (130, 704, 400, 64, 0.6),        # q8s: ragged last group (2 rows), N = 400 (partial tile)
+    (64, 8320, 272, 64, 0.5),        # split: kk = 4160, just past the q8s limit
 ]
 
 
@@ -194,17 +198,19 @@ def test_full_decode_chain(decode_q8, r):
 def test_workspace_reuse_and_graph_replay():
     """One zero-filled workspace serves consecutive calls of different sizes,
     and the chain captured in a HIP graph gives the eager result on every
-    replay (eager work and synchronisations between the replays)."""
-    M, K, N, gr = 64, 2048, 4096, 64
+    replay (eager work and synchronisations between the replays).  K = 8192:
+    r = 0.7 and 1 keep more than 4096 rows, so they run the split tiles that
+    meet through the workspace; r = 0.3 runs the shared-stream kernel."""
+    M, K, N, gr = 64, 8192, 4096, 64
     d = synth.linear_inputs("decode", M, K, N, seed=8)
     A = up_bf16(d["A"])
     Bq, s = rmm.rmm_quantize_q8(up_bf16(weight_bits(K, N, seed=3)))
     bn = rmm.rmm_rownorms_q8(Bq, s)
-    need = max(rmm.rmm_gemm_q8_workspace_bytes(M, N, rmm.rmm_kk(r, K), gr) for r in (0.3, 0.5, 1.0))
+    need = max(rmm.rmm_gemm_q8_workspace_bytes(M, N, rmm.rmm_kk(r, K), gr) for r in (0.3, 0.7, 1.0))
     assert need > 0
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     ref = {}
-    for r in (0.5, 0.3, 1.0, 0.5):
+    for r in (0.7, 0.3, 1.0, 0.7):
         kk = rmm.rmm_kk(r, K)
         idx = rmm.rmm_select(A, r, gr, bnorm=bn) if r < 1 else None
         Ap = rmm.rmm_gather(A, idx, kk, gr)[0] if r < 1 else A
@@ -213,8 +219,8 @@ def test_workspace_reuse_and_graph_replay():
         torch.cuda.synchronize()
         assert np.array_equal(down(Yw), down(Yf)), f"reused workspace differs at r={r}"
         ref[r] = down(Yf)
-    # graph: select -> gather -> GEMM at r = 0.5 on fixed buffers
-    r, kk = 0.5, rmm.rmm_kk(0.5, K)
+    # graph: select -> gather -> GEMM at r = 0.7 (split tiles) on fixed buffers
+    r, kk = 0.7, rmm.rmm_kk(0.7, K)
     idx = torch.zeros((1, rmm.rmm_kk_pad(kk)), dtype=torch.int32, device=DEV)
     Ap = torch.empty((M, rmm.rmm_kk_pad(kk)), dtype=torch.bfloat16, device=DEV)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
@@ -238,10 +244,10 @@ def test_workspace_reuse_and_graph_replay():
         Y.zero_()
         g.replay()
         torch.cuda.synchronize()
-        assert np.array_equal(down(Y), ref[0.5]), f"graph replay {rep} differs"
+        assert np.array_equal(down(Y), ref[0.7]), f"graph replay {rep} differs"
         step()   # eager work between replays
         torch.cuda.synchronize()
-        assert np.array_equal(down(Y), ref[0.5])
+        assert np.array_equal(down(Y), ref[0.7])
 
 
 def test_workspace_reuse_across_shapes():
@@ -249,8 +255,9 @@ def test_workspace_reuse_across_shapes():
     calls with different tile counts in any order (the arrival counters sit at
     the start of the workspace and are back at zero after every call, the
     partial sums at its end): each result equals the one from a fresh
-    zero-filled workspace."""
-    M, K, gr = 64, 1024, 64
+    zero-filled workspace.  K = 10240: kk = 5120 at r = 0.5, past the
+    shared-stream kernel's 4096, so every call runs split tiles."""
+    M, K, gr = 64, 10240, 64
     d = synth.linear_inputs("decode", M, K, 4096, seed=12)
     A = up_bf16(d["A"])
     shapes = [4096, 2048, 4096, 1024, 2048]
