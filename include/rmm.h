@@ -306,7 +306,9 @@ int rmm_rownorms_q8(const int8_t *Bq, int64_t ldq, const float *scale, int64_t K
 /* Workspace bytes rmm_gemm_q8 needs: 0, or, when the output has at most 128
  * tiles of 64 x 256 (each then split over two workgroups along the kept
  * rows), two fp32 64 x 256 partial tiles and one 4-byte arrival counter per
- * tile. */
+ * tile.  Calls with groups of at most 64 rows, kk <= 4096 and lda and ldidx
+ * of at least kk rounded up to 64 run a kernel without split tiles and leave
+ * the workspace untouched. */
 size_t rmm_gemm_q8_workspace_bytes(int64_t M, int64_t N, int64_t kk, int64_t group_rows);
 
 /* The reduced product on an int8 weight:

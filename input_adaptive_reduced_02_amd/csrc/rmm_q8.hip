@@ -522,9 +522,10 @@ k_gemm_q8(const uint16_t *__restrict__ A, int64_t lda, const int8_t *__restrict_
 // through a 4-stage DMA ring (3 slabs in flight), so there are no partial
 // sums to reduce and no split to hand off.  A short loop is where those fixed
 // costs of k_gemm_q8 weigh most: decode shape (64 x 8192 @ 8192 x 28672, same
-// box, identical outputs) 24.5 against 30.4 us at kk = 2458, 37.8 against
-// 39.6 us at kk = 4096; past that the per-slab widening and MFMAs no longer
-// hide under the stream (51.6 against 49.9 us at kk = 5735).
+// box) 24.5 against 30.4 us at kk = 2458, 37.8 against 39.6 us at kk = 4096;
+// past that the per-slab widening and MFMAs no longer hide under the stream
+// (51.6 against 49.9 us at kk = 5735).  The two kernels add the same exact
+// products in different fp32 orders.
 struct Q8sShape {
     static constexpr int TM = 64, TN = 128, BK = 64, NW = 4, WN = 32, FM = 2, KS = BK / 16;
     static constexpr int D = 3, NSTAGE = D + 1, IDX_RING = 2 * D;
