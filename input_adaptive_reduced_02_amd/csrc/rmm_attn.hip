@@ -430,12 +430,27 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
     } else {
         // ---------------------------------------------------------------- helper waves
         const int ht = tid - 256;
+        // Key loads and P stores go through buffer resources over one tile:
+        // the hardware range check (byte offset at or past num_records) makes
+        // a load read zeros and drops a store, which cuts the rows past the
+        // last key without per-lane compares. With L <= 32768 every offset
+        // stays below 2^31. Lane ht moves bytes 16 (ht & 15) of rows
+        // ht / 16 + 16 i, i = 0 .. 7.
+        const uint32_t kvoff = (uint32_t)ht * 16u;
+        const int qc = ht & 15;
+        // lanes whose query columns lie past the block's last query get an
+        // offset past any tile's num_records (0x80000000 + 7 * 32 L < 2^32)
+        const uint32_t pvoff = 8 * qc < nq ? (uint32_t)((ht >> 4) * L * 2 + 16 * qc) : 0x80000000u;
+        const uint32_t prow16 = (uint32_t)(16 * L * 2);
         u32x4 kreg[8];
-        if (U > 1) {
-            const int64_t k0 = (int64_t)tile_of(1) * kKT;
+        auto load_ktile = [&](int64_t k0) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(Kh + k0 * kHD), (short)0, (int)((L - k0) * kHD * 2), 0x00020000);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) kreg[i] = load_chunk(Kh, k0 + ((ht + 256 * i) >> 4), L, w);
-        }
+            for (int i = 0; i < 8; ++i)
+                kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, kvoff + 4096u * i, 0, 0));
+        };
+        if (U > 1) load_ktile((int64_t)tile_of(1) * kKT);
         __syncthreads();                               // prologue staging done
         for (int u = 0; u <= U; ++u) {
             if (u == T) __syncthreads();               // the compute waves' statistics exchange
@@ -444,11 +459,7 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                 uint16_t *kb = kbuf[(u + 1) & 1];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) *(u32x4 *)&kb[((ht + 256 * i) >> 4) * kPitch + 8 * w] = kreg[i];
-                if (u + 2 < U) {
-                    const int64_t kn0 = (int64_t)tile_of(u + 2) * kKT;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) kreg[i] = load_chunk(Kh, kn0 + ((ht + 256 * i) >> 4), L, w);
-                }
+                if (u + 2 < U) load_ktile((int64_t)tile_of(u + 2) * kKT);
             }
             if (u - 1 >= T) {
                 // the P tile of step u-1: every helper lane stores an eighth of
@@ -457,16 +468,17 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                 // pile onto two of the compute waves' SIMDs)
                 const uint16_t *pb = pbuf[(u - 1) & 1];
                 const int64_t kp0 = (int64_t)(u - 1 - T) * kKT;
-                auto store_tile = [&](int first, int stride, int n) {
-                    for (int i = 0; i < n; ++i) {
-                        const int c = first + stride * i, r = c >> 4, qc = c & 15;
-                        const int64_t k = kp0 + r;
-                        if (k < Kvalid && 8 * qc < nq)
-                            // non-temporal: P is written once and read by the next launch, so
-                            // it should not displace the K and Q tiles still being reused
-                            __builtin_nontemporal_store(*(const u32x4 *)&pb[r * kPitch + 8 * qc],
-                                                        (u32x4 *)(Pt + (h * L + k) * L + q0 + 8 * qc));
-                    }
+                auto store_tile = [&]() {
+                    const int64_t rows = Kvalid - kp0 < kKT ? Kvalid - kp0 : kKT;
+                    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                        (void *)(Pt + (h * L + kp0) * L + q0), (short)0, (int)(rows * L * 2), 0x00020000);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        // non-temporal (aux 2): P is written once and read by the next launch,
+                        // so it should not displace the K and Q tiles still being reused
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            *(const u32x4 *)&pb[((ht >> 4) + 16 * i) * kPitch + 8 * qc],
+                            rs, pvoff + prow16 * i, 0, 2);
                 };
                 if (PVS) {
                     // eight partial sums (query q mod 8), each in ascending q,
@@ -488,7 +500,7 @@ k_attn_probs(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, int
                     const double other = __shfl_xor(part, 1, 64);
                     if (hf == 0 && k < Kvalid) pvs[(h * G + g) * L + k] = (float)((part + other) * vnorm[h * L + k]);
                 }
-                store_tile(ht, 256, 8);
+                store_tile();
             }
             if (u < U) __syncthreads();
         }

@@ -105,7 +105,7 @@ def kernel_bodies(asm, part):
 # prefill GEMM's non-bf16 epilogue and the select kernels without a fused
 # gather have no such stream
 NT_STREAMS = [
-    ("rmm_attn.hip", "k_attn_probs", "global_store_dwordx4", True),
+    ("rmm_attn.hip", "k_attn_probs", "buffer_store_dwordx4", True),
     ("rmm_pv.hip", "k_pv_gemm", "global_load_lds_dwordx4", True),
     ("rmm_score.hip", "k_pv_mass", "global_load_dwordx4", True),
     ("rmm_gemm.hip", "k_gemm_sk", "global_load_lds_dwordx4", True),
