@@ -26,15 +26,6 @@ FROB_TOL = 5e-3
 ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
-def group_rows_sample(M, gr):
-    """Rows compared at full size: all of them for a single group, else the
-    first, the two middle and the last row of every group."""
-    if -(-M // gr) == 1:
-        return np.arange(M)
-    offs = (0, gr // 2 - 1, gr // 2, gr - 1)
-    return np.unique([min(M - 1, g * gr + o) for g in range(-(-M // gr)) for o in offs])
-
-
 def oracle_rows(A64, B64, idx, kk, gr, rows, A64abs=None, B64abs=None):
     """(Y, S) of the oracle's reduced product for the given rows, every column:
     Y the product, S the same sum over |a_k b_k| (the scale of the element
