@@ -27,7 +27,7 @@
  *     feature dimension of QK^T and the token dimension of PV ("Escopo de
  *     Aplicacao").
  *
- * Readings taken where the pages are silent (listed again in the design doc):
+ * Readings taken where the pages are silent:
  *   R1 score of slice k in group g = ||A[rows_g, k]||_2 * ||B[k, :]||_2.
  *      Passing b == NULL gives the pages' activation-only score.
  *   R2 selection is made per group of consecutive rows; a whole matrix is a
